@@ -1,0 +1,119 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module only draws and shapes random numbers; it holds none of the attention
+arithmetic, so both the fp64 oracle and the HIP path can take their inputs from it
+without sharing any of the method's code.
+
+The five named workloads are the ones the attention-forward benchmark is quoted on.
+The memory-budget exercise of "FlashAttention Interview Questions: IO Complexity,
+Tiling, and Numerical Stability" (section "Which complexity becomes smaller, and
+which does not?") uses N=4096, d=64 for one head, which is the ``c1`` workload.
+
+Draw order for every workload (all from one ``torch.Generator('cpu')`` seeded with
+the workload's seed): Q, K, V as float32 standard normals of shape [B, H, N, d];
+then (key padding only) one valid key length per batch element, an integer uniform
+on [N/2, N]; then (sampled-row checks only) for each (b, h) ``randperm(N)[:rows]``,
+sorted.  Q and K are multiplied by ``qk_gain`` before the cast to the input dtype
+(round to nearest even for bf16).
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KEY_PADDING = 2
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    in_dtype: torch.dtype
+    out_dtypes: tuple
+    mask_kinds: tuple          # each entry is a MASK_* bit set; the workload is run once per entry
+    seed: int
+    qk_gain: float = 1.0
+    sample_rows: Optional[int] = None   # rows per head the oracle checks at full size (None = all)
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        """Softmax scale 1/sqrt(d), as the float32 value the kernel receives."""
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+
+WORKLOADS = {
+    "c0": Workload("c0", 1, 1, 256, 64, torch.float32, (torch.float32,), (MASK_NONE,), seed=0,
+                   description="single head, fp32 inputs, no mask"),
+    "c1": Workload("c1", 1, 1, 4096, 64, torch.bfloat16, (torch.bfloat16, torch.float32),
+                   (MASK_NONE, MASK_CAUSAL), seed=1,
+                   description="memory-budget example N=4096 d=64; non-causal and causal; bf16 and fp32 out"),
+    "c2": Workload("c2", 4, 16, 8192, 128, torch.bfloat16, (torch.bfloat16,), (MASK_CAUSAL,), seed=2,
+                   sample_rows=256, description="batched causal, the throughput/roofline workload"),
+    "c3": Workload("c3", 2, 32, 16384, 64, torch.bfloat16, (torch.bfloat16,), (MASK_KEY_PADDING,), seed=3,
+                   qk_gain=3.0, sample_rows=256,
+                   description="key padding, Q and K x3 so logit std ~ 9"),
+    "c4": Workload("c4", 1, 8, 131072, 128, torch.bfloat16, (torch.bfloat16,), (MASK_CAUSAL,), seed=4,
+                   sample_rows=1024, description="long-context causal, 1024 sampled rows per head"),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    q: torch.Tensor          # [B,H,N,d] CPU, in_dtype
+    k: torch.Tensor
+    v: torch.Tensor
+    seqlens: Optional[torch.Tensor]   # [B] int32 CPU, or None
+    rows: Optional[torch.Tensor]      # [B,H,R] int64 CPU sorted, or None
+    scale: float
+
+
+def random_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
+               qk_gain: float = 1.0):
+    """Q, K, V standard normals (Q, K times ``qk_gain``) cast to ``dtype``; CPU tensors."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    k = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    if qk_gain != 1.0:
+        q.mul_(qk_gain)
+        k.mul_(qk_gain)
+    return q.to(dtype), k.to(dtype), v.to(dtype), g
+
+
+def draw_seqlens(g: torch.Generator, B: int, N: int) -> torch.Tensor:
+    """One valid key length per batch element, integer uniform on [N/2, N]."""
+    return torch.randint(N // 2, N + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def draw_rows(g: torch.Generator, B: int, H: int, N: int, R: int) -> torch.Tensor:
+    """For each (b, h), R distinct query rows chosen by ``randperm``, sorted."""
+    out = torch.empty(B, H, min(R, N), dtype=torch.int64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = torch.sort(torch.randperm(N, generator=g)[:R]).values
+    return out
+
+
+def make_inputs(w: Workload, mask_kind: Optional[int] = None, sample_rows: Optional[int] = None) -> Inputs:
+    """Inputs of workload ``w`` in the documented draw order."""
+    q, k, v, g = random_qkv(w.B, w.H, w.N, w.d, w.in_dtype, w.seed, w.qk_gain)
+    mk = w.mask_kinds[0] if mask_kind is None else mask_kind
+    seqlens = draw_seqlens(g, w.B, w.N) if (mk & MASK_KEY_PADDING) else None
+    R = w.sample_rows if sample_rows is None else sample_rows
+    rows = draw_rows(g, w.B, w.H, w.N, R) if R is not None else None
+    return Inputs(q, k, v, seqlens, rows, w.scale)
+
+
+def scale_for(d: int) -> float:
+    """1/sqrt(d) rounded to float32, the value passed across the C ABI."""
+    return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())

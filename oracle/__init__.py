@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for exact attention -- TEST INFRASTRUCTURE.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  It shares no code with the HIP path and never imports it.
+"""
+
+from .attention import attention_ref, online_ref, brute_ref, softmax_weights_ref, visible_keys  # noqa: F401
+from . import accounting  # noqa: F401
