@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused exact-attention forward on one MI355X.
+
+One step = one fused forward (one kernel launch) over the whole workload, inputs already
+resident in device memory.  Prints one JSON line:
+
+  value      whole-job throughput in TFLOP/s, counting 4*B*H*N^2*d FLOP per forward
+             (halved under the causal mask);
+  roofline   the kernel's achieved TFLOP/s per launch (same FLOP count / the average launch
+             duration, timed with HIP events on the launch stream) against the MI355X dense
+             bf16 MFMA peak, plus HBM traffic per launch from rocprofv3 FETCH_SIZE/WRITE_SIZE
+             counters when the recorded counters match the current kernel sources;
+  cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of the same
+             workload (seed-chosen query rows of every head), scaled to TFLOP/s.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4k–128k, d=64/128, 1 GPU"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.txt")
+KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_f32.h", "fa_sched.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for s in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_tiled_attention_19_amd", "csrc", s), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def counted_flops(B, H, N, d, causal) -> float:
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
+    summary is absent, is for another workload, or predates the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("workload") != workload or vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, rows_per_head: int):
+    """Time the fp64 oracle on `rows_per_head` seed-chosen query rows of every head."""
+    import numpy as np  # noqa: F401
+    import torch
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    g = torch.Generator("cpu").manual_seed(12345)
+    rows = torch.stack([torch.stack([torch.sort(torch.randperm(w.N, generator=g)[:rows_per_head]).values
+                                     for _ in range(w.H)]) for _ in range(w.B)])
+    causal = bool(w.mask_kinds[0] & 1)
+    seq = x.seqlens.tolist() if x.seqlens is not None else None
+    t0 = time.perf_counter()
+    oracle.attention_ref(x.q, x.k, x.v, x.scale, causal=causal, seqlens=seq, rows=rows)
+    dt = time.perf_counter() - t0
+    # counted FLOP of the sampled rows: each row carries 4*d*(keys it is charged for); the
+    # causal convention charges a row N/2 keys on average, so a uniform sample of R rows per
+    # head carries R/N of the whole workload's counted FLOP.
+    frac = rows_per_head / w.N
+    flops = counted_flops(w.B, w.H, w.N, w.d, causal) * frac
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows_per_head} seed-chosen query rows of each of the {w.B * w.H} heads "
+                      f"({frac:.4%} of the workload's counted FLOP), fp64 numpy, {dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, the roofline workload)")
+    ap.add_argument("--mask", type=int, default=None, help="override the workload's mask bits")
+    ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
+    ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the forward pass shards over (batch, head) with no "
+              f"communication, so multi-GPU throughput is N x the one-GPU value by construction "
+              f"and is not measured here.", file=sys.stderr)
+        return 2
+
+    import torch
+    import exact_tiled_attention_19_amd as fa
+    from exact_tiled_attention_19_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    fa.load_library()
+    w = W.WORKLOADS[args.workload]
+    mask = w.mask_kinds[0] if args.mask is None else args.mask
+    causal = bool(mask & W.MASK_CAUSAL)
+    out_dtype = w.out_dtypes[0] if args.out_dtype is None else (
+        torch.bfloat16 if args.out_dtype == "bf16" else torch.float32)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    x = W.make_inputs(w, mask_kind=mask)
+    dev = torch.device("cuda", 0)
+    q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+    seq = x.seqlens.to(dev) if (mask & W.MASK_KEY_PADDING) else None
+    o = torch.empty(q.shape, dtype=out_dtype, device=dev)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        fa.forward(q, k, v, scale=x.scale, causal=causal, seqlens=seq, out_dtype=out_dtype,
+                   out=o, lse_out=lse, variant=args.variant)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+
+    flops = counted_flops(w.B, w.H, w.N, w.d, causal)
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / avg_launch_s / 1e12
+    fp32 = w.in_dtype == torch.float32
+    peak = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    mask_name = {0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[mask]
+    workload_id = f"{w.name}:{mask_name}:{'f32' if out_dtype == torch.float32 else 'bf16'}-out"
+    traffic = recorded_traffic(workload_id)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if fp32 else "bf16",
+        "data": "synthetic (seeded normal Q, K, V of the workload's shape; no dataset)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {mask_name} mask, "
+                        f"{'fp32' if fp32 else 'bf16'} in, "
+                        f"{'fp32' if out_dtype == torch.float32 else 'bf16'} out, fp32 LSE",
+            "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name,
+            "flop_per_step": flops, "variant": args.variant,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 5),
+            "traffic": traffic,
+            "kernel_avg_ms": round(avg_launch_s * 1e3, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] timing the fp64 oracle on {args.cpu_rows} rows per head", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_rows, w.N))
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

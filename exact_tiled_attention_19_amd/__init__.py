@@ -1,0 +1,27 @@
+"""Fused exact-attention forward for AMD Instinct MI355X (gfx950).
+
+``forward(q, k, v, ...)`` runs the HIP kernels of ``libfa.so`` through its C ABI
+(include/fa.h); PyTorch only supplies device memory and the stream.
+"""
+
+from .binding import (  # noqa: F401
+    FA_DTYPE_BF16,
+    FA_DTYPE_F32,
+    FA_ERR_HIP,
+    FA_ERR_INVALID_ARG,
+    FA_ERR_UNSUPPORTED,
+    FA_MASK_CAUSAL,
+    FA_MASK_KEY_PADDING,
+    FA_MASK_NONE,
+    FA_OK,
+    FaError,
+    FaInvalidArgument,
+    FaUnsupported,
+    LIB_PATH,
+    fa_fwd,
+    forward,
+    load_library,
+    status_str,
+    variant_count,
+    version,
+)

@@ -1,0 +1,170 @@
+"""Thin ctypes binding of ``libfa.so`` (the C ABI in include/fa.h).
+
+Argument marshalling only: PyTorch provides device memory and the current HIP stream; every
+step of the attention forward runs in the library's HIP kernels.  There is no fallback: if
+the library is missing or cannot be loaded, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+
+FA_OK = 0
+FA_ERR_INVALID_ARG = 1
+FA_ERR_UNSUPPORTED = 2
+FA_ERR_HIP = 3
+
+FA_MASK_NONE = 0
+FA_MASK_CAUSAL = 1
+FA_MASK_KEY_PADDING = 2
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+
+_DTYPE_CODE = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16}
+
+# Every symbol include/fa.h declares, with its ctypes signature.
+_VP = ctypes.c_void_p
+_I = ctypes.c_int
+SIGNATURES = {
+    "fa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP]),
+    "fa_fwd_variant": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP, _I]),
+    "fa_variant_count": (_I, []),
+    "fa_status_str": (ctypes.c_char_p, [_I]),
+    "fa_last_hip_error": (_I, []),
+    "fa_version": (_I, []),
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class FaInvalidArgument(FaError, ValueError):
+    pass
+
+
+class FaUnsupported(FaError, ValueError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and return the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m exact_tiled_attention_19_amd.build_lib` (needs hipcc)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().fa_status_str(status).decode()
+
+
+def _check(status: int) -> None:
+    if status == FA_OK:
+        return
+    lib = load_library()
+    msg = lib.fa_status_str(status).decode()
+    if status == FA_ERR_INVALID_ARG:
+        raise FaInvalidArgument(status, msg)
+    if status == FA_ERR_UNSUPPORTED:
+        raise FaUnsupported(status, msg)
+    if status == FA_ERR_HIP:
+        raise FaError(status, f"{msg}: hipError_t {lib.fa_last_hip_error()}")
+    raise FaError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, in_dtype, out_dtype, stream,
+           variant: int = 0) -> int:
+    """Raw call through the C ABI (pointers as ints or None); returns the status code."""
+    lib = load_library()
+    if variant == 0:
+        return lib.fa_fwd(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), mask_kind, seqlens,
+                          in_dtype, out_dtype, stream)
+    return lib.fa_fwd_variant(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), mask_kind, seqlens,
+                              in_dtype, out_dtype, stream, variant)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+            causal: bool = False, seqlens: Optional[torch.Tensor] = None,
+            out_dtype: Optional[torch.dtype] = None, return_lse: bool = True,
+            out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+            variant: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact attention forward on the GPU: returns (O, LSE).
+
+    q, k, v: [B, H, N, d] contiguous device tensors of one dtype (bfloat16 or float32).
+    scale: multiplier of q.k (default 1/sqrt(d), rounded to float32).
+    causal: key j visible to query i only when j <= i.
+    seqlens: optional int32 device tensor [B]; keys j >= seqlens[b] are masked.
+    out_dtype: output dtype (default: the input dtype).
+    out / lse_out: optional preallocated outputs.
+    """
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dtype != k.dtype or q.dtype != v.dtype or q.dtype not in _DTYPE_CODE:
+        raise ValueError("q, k, v must share a dtype in {bfloat16, float32}")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape:
+        raise ValueError("q, k, v must all be [B, H, N, d]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
+    if seqlens is not None:
+        if not seqlens.is_cuda or seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 device tensor with B entries")
+        mask |= FA_MASK_KEY_PADDING
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    lse = None
+    if return_lse:
+        if lse_out is None:
+            lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        else:
+            if lse_out.shape != (B, H, N) or lse_out.dtype != torch.float32 or not lse_out.is_contiguous():
+                raise ValueError("lse_out must be a contiguous float32 [B, H, N] tensor")
+            lse = lse_out
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, float(scale), mask,
+                _ptr(seqlens), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype], stream, variant)
+    _check(st)
+    return out, lse
+
+
+def variant_count() -> int:
+    return load_library().fa_variant_count()
+
+
+def version() -> int:
+    return load_library().fa_version()

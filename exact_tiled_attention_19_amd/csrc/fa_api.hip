@@ -1,0 +1,163 @@
+// C ABI of the fused attention forward (declared in include/fa.h): host-side validation,
+// kernel selection and launch.  No allocation, no synchronisation, no state except the
+// thread-local last HIP error.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/fa.h"
+#include "fa_fwd_bf16.h"
+#include "fa_fwd_f32.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kBM = 128;       // query rows per workgroup (all kernels)
+constexpr int kThreads = 256;  // 4 wave64s per workgroup
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+using Kernel = void (*)(fa::FwdArgs);
+
+// Variant 0: the production kernel.  Variant 1: the same kernel gathering the V^T operand
+// with 16-bit LDS reads instead of LDS transpose reads.
+constexpr int kNumVariants = 2;
+
+template <int D, bool CAUSAL, bool PAD, bool OUTF32>
+Kernel pick_bf16_vt(int variant) {
+    return variant == 0 ? fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>
+                        : fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>;
+}
+
+template <int D, bool OUTF32>
+Kernel pick_bf16_mask(int mask, int variant) {
+    switch (mask) {
+        case 0: return pick_bf16_vt<D, false, false, OUTF32>(variant);
+        case 1: return pick_bf16_vt<D, true, false, OUTF32>(variant);
+        case 2: return pick_bf16_vt<D, false, true, OUTF32>(variant);
+        default: return pick_bf16_vt<D, true, true, OUTF32>(variant);
+    }
+}
+
+template <int D>
+Kernel pick_f32_mask(int mask) {
+    switch (mask) {
+        case 0: return fa::fa_fwd_f32_kernel<D, false, false>;
+        case 1: return fa::fa_fwd_f32_kernel<D, true, false>;
+        case 2: return fa::fa_fwd_f32_kernel<D, false, true>;
+        default: return fa::fa_fwd_f32_kernel<D, true, true>;
+    }
+}
+
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype, int out_dtype,
+           void* stream, int variant) {
+    // ---- validation (host only, before any HIP call) ----
+    if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
+    if (mask_kind < 0 || mask_kind > (FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (out_dtype != FA_DTYPE_F32 && out_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (d <= 0) return FA_ERR_INVALID_ARG;
+    if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_DTYPE_F32 && out_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    if (in_dtype == FA_DTYPE_F32 && variant != 0) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+    if ((mask_kind & FA_MASK_KEY_PADDING) && !seqlens) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
+    if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
+    if ((mask_kind & FA_MASK_KEY_PADDING) && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
+    // sizes: element offsets are 64-bit in the kernels; workgroup counts must fit in int
+    const int64_t n_qtiles = (static_cast<int64_t>(N) + kBM - 1) / kBM;
+    const int64_t total = static_cast<int64_t>(B) * H * n_qtiles;
+    if (total > 0x7fffffff || static_cast<int64_t>(B) * H > 0x7fffffff) return FA_ERR_INVALID_ARG;
+    const size_t in_bytes = static_cast<size_t>(B) * H * N * d * (in_dtype == FA_DTYPE_F32 ? 4 : 2);
+    const size_t out_bytes = static_cast<size_t>(B) * H * N * d * (out_dtype == FA_DTYPE_F32 ? 4 : 2);
+    if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) ||
+        overlaps(o, out_bytes, v, in_bytes))
+        return FA_ERR_INVALID_ARG;
+    if (lse && (overlaps(lse, static_cast<size_t>(B) * H * N * 4, o, out_bytes) ||
+                overlaps(lse, static_cast<size_t>(B) * H * N * 4, q, in_bytes) ||
+                overlaps(lse, static_cast<size_t>(B) * H * N * 4, k, in_bytes) ||
+                overlaps(lse, static_cast<size_t>(B) * H * N * 4, v, in_bytes)))
+        return FA_ERR_INVALID_ARG;
+
+    // ---- kernel selection ----
+    const int mask = mask_kind;
+    Kernel kern = nullptr;
+    if (in_dtype == FA_DTYPE_BF16) {
+        const bool of32 = out_dtype == FA_DTYPE_F32;
+        if (d == 64) kern = of32 ? pick_bf16_mask<64, true>(mask, variant) : pick_bf16_mask<64, false>(mask, variant);
+        else kern = of32 ? pick_bf16_mask<128, true>(mask, variant) : pick_bf16_mask<128, false>(mask, variant);
+    } else {
+        kern = d == 64 ? pick_f32_mask<64>(mask) : pick_f32_mask<128>(mask);
+    }
+
+    fa::FwdArgs args;
+    args.q = q;
+    args.k = k;
+    args.v = v;
+    args.o = o;
+    args.lse = lse;
+    args.seqlens = (mask_kind & FA_MASK_KEY_PADDING) ? seqlens : nullptr;
+    args.B = B;
+    args.H = H;
+    args.N = N;
+    args.n_qtiles = static_cast<int>(n_qtiles);
+    args.total_wgs = static_cast<int>(total);
+    args.scale = scale;
+    args.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(total)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), args);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return FA_ERR_HIP;
+    }
+    return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype, int out_dtype,
+           void* stream) {
+    return launch(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, in_dtype, out_dtype, stream, 0);
+}
+
+int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype,
+                   int out_dtype, void* stream, int variant) {
+    return launch(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, in_dtype, out_dtype, stream,
+                  variant);
+}
+
+int fa_variant_count(void) { return kNumVariants; }
+
+const char* fa_status_str(int status) {
+    switch (status) {
+        case FA_OK: return "FA_OK: success";
+        case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+        case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this head width, dtype pair or variant";
+        case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed (see fa_last_hip_error)";
+        default: return "unknown fa_status";
+    }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+int fa_version(void) { return FA_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// Work mapping of the forward kernels: workgroup id -> (batch*head, query tile).
+//
+// Plain C++ (no HIP types) so the host test suite can compile it with g++ and check that
+// the mapping is a bijection.  Under hipcc the functions are also device functions.
+#pragma once
+
+#if defined(__HIPCC__)
+#define FA_HD __host__ __device__
+#else
+#define FA_HD
+#endif
+
+namespace fa {
+
+// MI355X has 8 accelerator complex dies (XCDs), each with its own L2.  The dispatcher hands
+// consecutive workgroup ids to the XCDs round-robin, so id w runs on XCD (w % 8).  Remapping
+// makes the logical work items one XCD receives contiguous: all query tiles of one head then
+// run on the same XCD and reuse that head's K/V tiles from its L2.
+constexpr int kNumXcd = 8;
+
+FA_HD inline int xcd_remap(int wg, int total) {
+    const int per = (total + kNumXcd - 1) / kNumXcd;  // items on the fuller XCDs
+    int full = total % kNumXcd;                        // XCDs that hold `per` items
+    if (full == 0) full = kNumXcd;
+    const int xcd = wg % kNumXcd;
+    const int local = wg / kNumXcd;
+    return xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
+}
+
+struct TileCoord {
+    int bh;  // b * H + h
+    int qt;  // query tile index
+};
+
+// Logical item -> (head, query tile).  Items of one head are contiguous.  With a causal mask
+// the tiles of a head are visited from the last (most keys, most work) to the first, so the
+// long tiles start early and the short ones fill the tail of the launch.
+FA_HD inline TileCoord tile_of(int logical, int n_qtiles, bool causal) {
+    TileCoord t;
+    t.bh = logical / n_qtiles;
+    const int r = logical - t.bh * n_qtiles;
+    t.qt = causal ? (n_qtiles - 1 - r) : r;
+    return t;
+}
+
+}  // namespace fa

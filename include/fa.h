@@ -1,0 +1,111 @@
+/*
+ * fa.h -- C ABI of the fused exact-attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The operation is exact attention for every (batch b, head h):
+ *
+ *     O = softmax(Q K^T * scale + mask) V,    LSE_i = ln sum_{j visible to i} exp(scale * q_i . k_j)
+ *
+ * as defined in "FlashAttention Interview Questions: IO Complexity, Tiling, and Numerical
+ * Stability" (cswork.org), section "What is FlashAttention exact about?" (scores = Q K^T /
+ * sqrt(d); weights = row_softmax(scores + mask); output = weights V, one head of length N and
+ * width d).  It is computed tile by tile with running row statistics -- the update of the same
+ * page's section "How can softmax be computed across tiles?" -- inside one kernel, so the
+ * N x N score matrix never exists in device memory ("FlashAttention 1, 2 & 3: Memory Tiling &
+ * Eliminating the O(N^2) HBM Bottleneck", section 2, "Kernel Fusion").  The log-sum-exp is the
+ * compact per-row normalisation information that a backward pass needs (cswork.org page,
+ * section "Why can recomputation help training?").
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates,
+ *     frees and synchronises nothing and keeps no state between calls except a thread-local
+ *     copy of the last HIP error.  Work is enqueued on `stream` (a hipStream_t; NULL means the
+ *     default stream) and the call returns without waiting for it.
+ *   - Layout: Q, K, V and O are [B, H, N, d] contiguous row-major (d fastest); LSE is [B, H, N].
+ *   - Masks (bit flags, FA_MASK_*): under FA_MASK_CAUSAL key j is visible to query i only when
+ *     j <= i (square, aligned positions).  Under FA_MASK_KEY_PADDING key j of batch element b is
+ *     visible only when j < seqlens[b] (values are clamped to [0, N]); query rows are never
+ *     masked.  Masked scores are replaced (not offset) so they carry exactly zero weight, and
+ *     extreme finite values stored at masked K/V positions do not change any visible output.
+ *   - A row with no visible key (only possible when seqlens[b] == 0) gets O = 0 and LSE = -inf,
+ *     never NaN (the cswork.org page asks that this case be defined: section "Does subtracting
+ *     the maximum solve every numerical issue?").
+ *   - Arguments are validated on the host before any HIP call; nothing is launched when a check
+ *     fails.  B, H or N equal to 0 is a no-op that returns FA_OK.
+ *   - NaN or infinite values in Q, K or V are outside the contract.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_VERSION 10000 /* major*10000 + minor*100 + patch */
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, unknown mask bit, padding without
+                                seqlens, scale negative or not finite, misaligned pointer,
+                                O aliasing an input, size overflow */
+    FA_ERR_UNSUPPORTED = 2,  /* valid arguments this build has no kernel for (d, dtype pair) */
+    FA_ERR_HIP = 3           /* the launch failed; fa_last_hip_error() gives the hipError_t */
+} fa_status;
+
+enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_KEY_PADDING = 2 };
+enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 };
+
+/*
+ * fa_fwd -- the fused forward pass.
+ *
+ *   q, k, v   [B, H, N, d] device tensors of `in_dtype`, 16-byte aligned.
+ *   o         [B, H, N, d] device tensor of `out_dtype`, 16-byte aligned; written.  Must not
+ *             overlap q, k or v.
+ *   lse       [B, H, N] float32 device tensor, 4-byte aligned, natural-log log-sum-exp of the
+ *             visible scaled scores; written.  NULL: not stored.
+ *   B, H, N   batch, heads, sequence length (>= 0).  d: head width.
+ *   scale     multiplier of every dot product (finite, >= 0; normally 1/sqrt(d)).
+ *   mask_kind FA_MASK_* bits (0..3).
+ *   seqlens   device int32[B], valid key length per batch element; required iff
+ *             FA_MASK_KEY_PADDING is set, ignored otherwise.
+ *   in_dtype, out_dtype   supported pairs: (BF16, BF16) and (BF16, F32) with d in {64, 128};
+ *             (F32, F32) with d in {64, 128}.  Products take bf16 operands with float32
+ *             accumulation; with a float32 output the probabilities enter the value product
+ *             as a two-term bf16 split, so their rounding stays below 2^-16 relative.
+ *             float32 inputs are multiplied in float32 throughout.
+ *   stream    hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Returns an fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
+           int in_dtype, int out_dtype, void* stream);
+
+/*
+ * fa_fwd_variant -- fa_fwd with an explicit kernel variant, for tests and tuning only.
+ * variant 0 is what fa_fwd runs.  Other values select alternative, equally exact
+ * implementations of the same operation (see fa_variant_count); every variant must pass the
+ * same parity tests.  An unknown variant returns FA_ERR_UNSUPPORTED.
+ */
+int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
+                   int in_dtype, int out_dtype, void* stream, int variant);
+
+/* Number of kernel variants fa_fwd_variant accepts (variants are 0 .. count-1). */
+int fa_variant_count(void);
+
+/* Static, never-NULL description of a status code (unknown codes get a generic string). */
+const char* fa_status_str(int status);
+
+/* hipError_t behind the most recent FA_ERR_HIP returned on this thread (0 if none). */
+int fa_last_hip_error(void);
+
+/* FA_VERSION of the built library. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,165 @@
+"""CPU tests of the C ABI boundary and the host-side logic (no GPU work is launched).
+
+* libfa.so loads and exports every function include/fa.h declares.
+* Every invalid argument is rejected on the host with the documented status before any HIP
+  call (the arguments below always fail validation, so nothing reaches the GPU).
+* The workgroup -> (head, query tile) mapping is a bijection (host compile of fa_sched.h).
+"""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_tiled_attention_19_amd as fa
+from exact_tiled_attention_19_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+F32, BF16 = fa.FA_DTYPE_F32, fa.FA_DTYPE_BF16
+P = 0x10000          # a 16-byte-aligned stand-in address; validation fails before any use
+P2 = 0x40000000
+P3 = 0x80000000
+P4 = 0xC0000000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_api():
+    assert declared_functions() == sorted(binding.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (fa_\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_matches_header():
+    m = re.search(r"#define FA_VERSION (\d+)", open(HEADER).read())
+    assert fa.version() == int(m.group(1))
+
+
+def test_status_strings():
+    lib = fa.load_library()
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_HIP):
+        s = lib.fa_status_str(code)
+        assert s and s.decode().startswith(("FA_OK", "FA_ERR"))
+    assert lib.fa_status_str(12345).decode() == "unknown fa_status"
+    assert lib.fa_status_str(-1)
+    assert lib.fa_last_hip_error() == 0
+    assert fa.variant_count() >= 1
+
+
+def call(q=P, k=P2, v=P3, o=P4, lse=None, B=1, H=1, N=16, d=64, scale=0.125, mask=0, seqlens=None,
+         ind=BF16, outd=BF16, variant=0):
+    return fa.fa_fwd(q, k, v, o, lse, B, H, N, d, scale, mask, seqlens, ind, outd, None, variant)
+
+
+INVALID = {
+    "null q": dict(q=None),
+    "null k": dict(k=None),
+    "null v": dict(v=None),
+    "null o": dict(o=None),
+    "negative B": dict(B=-1),
+    "negative H": dict(H=-2),
+    "negative N": dict(N=-16),
+    "mask bit 4": dict(mask=4),
+    "mask -1": dict(mask=-1),
+    "padding without seqlens": dict(mask=fa.FA_MASK_KEY_PADDING),
+    "causal+padding without seqlens": dict(mask=3),
+    "nan scale": dict(scale=float("nan")),
+    "inf scale": dict(scale=float("inf")),
+    "negative scale": dict(scale=-0.125),
+    "misaligned q": dict(q=P + 2),
+    "misaligned k": dict(k=P2 + 8),
+    "misaligned v": dict(v=P3 + 4),
+    "misaligned o": dict(o=P4 + 2),
+    "misaligned lse": dict(lse=P4 + (1 << 24) + 2),
+    "misaligned seqlens": dict(mask=2, seqlens=P4 + (1 << 24) + 1),
+    "o aliases q": dict(o=P),
+    "o overlaps v": dict(o=P3 + 16),
+    "lse inside o": dict(lse=P4 + 64),
+    "bad in dtype": dict(ind=7),
+    "bad out dtype": dict(outd=-1),
+    "d zero": dict(d=0),
+    "too many workgroups": dict(B=1 << 20, H=1 << 10, N=1 << 20),
+}
+
+UNSUPPORTED = {
+    "d 32": dict(d=32),
+    "d 96": dict(d=96),
+    "d 256": dict(d=256),
+    "f32 in bf16 out": dict(ind=F32, outd=BF16),
+    "unknown variant": dict(variant=99),
+    "negative variant": dict(variant=-1),
+    "f32 with variant 1": dict(ind=F32, outd=F32, variant=1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(INVALID))
+def test_invalid_argument_rejected_on_host(name):
+    assert call(**INVALID[name]) == fa.FA_ERR_INVALID_ARG, name
+
+
+@pytest.mark.parametrize("name", sorted(UNSUPPORTED))
+def test_unsupported_rejected_on_host(name):
+    assert call(**UNSUPPORTED[name]) == fa.FA_ERR_UNSUPPORTED, name
+
+
+@pytest.mark.parametrize("dims", [(0, 1, 16), (1, 0, 16), (1, 1, 0), (0, 0, 0)])
+def test_empty_problem_is_a_noop(dims):
+    B, H, N = dims
+    # null pointers are fine for an empty problem: nothing is read, written or launched
+    assert fa.fa_fwd(None, None, None, None, None, B, H, N, 64, 0.125, 0, None, BF16, BF16, None) == fa.FA_OK
+    assert fa.fa_fwd(None, None, None, None, None, B, H, N, 128, 0.125, 3, None, BF16, F32, None) == fa.FA_OK
+
+
+def test_python_forward_rejects_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.forward(x, x, x)
+
+
+def test_sched_mapping_is_bijective(tmp_path):
+    """Host compile of the work-mapping header: every logical item is visited once."""
+    src = tmp_path / "sched_test.cpp"
+    src.write_text(
+        '#include "fa_sched.h"\n#include <cstdio>\n#include <vector>\n'
+        "int main() {\n"
+        "  int bad = 0;\n"
+        "  for (int total = 1; total <= 3000; ++total) {\n"
+        "    std::vector<int> seen(total, 0);\n"
+        "    for (int w = 0; w < total; ++w) { int l = fa::xcd_remap(w, total);\n"
+        "      if (l < 0 || l >= total) { ++bad; continue; } ++seen[l]; }\n"
+        "    for (int i = 0; i < total; ++i) if (seen[i] != 1) ++bad;\n"
+        "    // items that share an XCD are contiguous in logical order\n"
+        "    for (int w = 8; w < total; ++w) if (fa::xcd_remap(w, total) != fa::xcd_remap(w - 8, total) + 1) ++bad;\n"
+        "  }\n"
+        "  for (int nq : {1, 2, 7, 64}) for (int causal = 0; causal < 2; ++causal) {\n"
+        "    std::vector<int> seen(3 * nq, 0);\n"
+        "    for (int l = 0; l < 3 * nq; ++l) { fa::TileCoord t = fa::tile_of(l, nq, causal);\n"
+        "      if (t.qt < 0 || t.qt >= nq || t.bh < 0 || t.bh >= 3) { ++bad; continue; } ++seen[t.bh * nq + t.qt]; }\n"
+        "    for (int x : seen) if (x != 1) ++bad;\n"
+        "    if (causal && fa::tile_of(0, nq, true).qt != nq - 1) ++bad;\n"
+        "  }\n"
+        '  std::printf("bad=%d\\n", bad);\n'
+        "  return bad != 0;\n"
+        "}\n")
+    exe = tmp_path / "sched_test"
+    inc = os.path.join(ROOT, "exact_tiled_attention_19_amd", "csrc")
+    subprocess.run(["g++", "-std=c++17", "-O1", "-I", inc, str(src), "-o", str(exe)], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout + r.stderr

@@ -1,0 +1,125 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+* Small seeded cases that span several 128-row query tiles and 64-key tiles plus ragged
+  tails, for every head width, mask kind, output dtype and kernel variant.
+* The five named workloads: c0 and c1 in full; c2, c3 and c4 at their full sizes in the same
+  launch configuration the benchmark times, checked on seed-chosen sampled query rows.
+"""
+
+import sys
+
+import pytest
+import torch
+
+import exact_tiled_attention_19_amd as fa
+from exact_tiled_attention_19_amd import workloads as W
+from tests.parity_util import check_case
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    fa.load_library()   # fail loudly when the HIP library is missing
+
+
+def _report(label, res):
+    print(f"[parity] {label}: " + ", ".join(f"{k}={v:.3e}" for k, v in res.items()), flush=True)
+
+
+MASKS = {"none": (False, False), "causal": (True, False), "pad": (False, True), "causal_pad": (True, True)}
+
+
+def _seqlens(B, N, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randint(1, N + 1, (B,), generator=g, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 300, 1000])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_sweep_bf16(N, d, mask):
+    causal, pad = MASKS[mask]
+    B, H = 2, 2
+    q, k, v, _ = W.random_qkv(B, H, N, d, BF16, seed=1000 + N + d)
+    seq = _seqlens(B, N, N + 7) if pad else None
+    for out_dtype in (BF16, F32):
+        label = f"N={N} d={d} mask={mask} out={out_dtype}"
+        print(f"[case] {label}", flush=True)
+        _report(label, check_case(q, k, v, scale=W.scale_for(d), causal=causal, seqlens=seq,
+                                  out_dtype=out_dtype, label=label))
+
+
+@pytest.mark.parametrize("variant", range(1, 2))
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_variants_bf16(variant, d, mask):
+    causal, pad = MASKS[mask]
+    B, H, N = 1, 3, 333
+    q, k, v, _ = W.random_qkv(B, H, N, d, BF16, seed=77 + d)
+    seq = _seqlens(B, N, 5) if pad else None
+    for out_dtype in (BF16, F32):
+        label = f"variant={variant} d={d} mask={mask} out={out_dtype}"
+        print(f"[case] {label}", flush=True)
+        _report(label, check_case(q, k, v, scale=W.scale_for(d), causal=causal, seqlens=seq,
+                                  out_dtype=out_dtype, variant=variant, label=label))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 31, 32, 33, 200, 256, 511])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_sweep_f32(N, d, mask):
+    causal, pad = MASKS[mask]
+    B, H = 1, 2
+    q, k, v, _ = W.random_qkv(B, H, N, d, F32, seed=2000 + N + d)
+    seq = _seqlens(B, N, N + 3) if pad else None
+    label = f"f32 N={N} d={d} mask={mask}"
+    print(f"[case] {label}", flush=True)
+    _report(label, check_case(q, k, v, scale=W.scale_for(d), causal=causal, seqlens=seq,
+                              out_dtype=F32, label=label))
+
+
+@pytest.mark.parametrize("scale", [0.0, 1.0, 0.05])
+def test_other_scales(scale):
+    q, k, v, _ = W.random_qkv(1, 2, 200, 64, BF16, seed=9)
+    for causal in (False, True):
+        label = f"scale={scale} causal={causal}"
+        _report(label, check_case(q, k, v, scale=scale, causal=causal, out_dtype=F32, label=label))
+
+
+# ------------------------------------------------------------------ named workloads
+
+def test_workload_c0():
+    w = W.WORKLOADS["c0"]
+    x = W.make_inputs(w)
+    _report("c0", check_case(x.q, x.k, x.v, scale=x.scale, out_dtype=F32, label="c0"))
+
+
+@pytest.mark.parametrize("mask", [W.MASK_NONE, W.MASK_CAUSAL])
+@pytest.mark.parametrize("out_dtype", [BF16, F32])
+def test_workload_c1(mask, out_dtype):
+    w = W.WORKLOADS["c1"]
+    x = W.make_inputs(w, mask_kind=mask)
+    label = f"c1 mask={mask} out={out_dtype}"
+    _report(label, check_case(x.q, x.k, x.v, scale=x.scale, causal=bool(mask & W.MASK_CAUSAL),
+                              out_dtype=out_dtype, label=label))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_workload_full_size_sampled_rows(name):
+    w = W.WORKLOADS[name]
+    print(f"[case] {name}: generating inputs", flush=True)
+    x = W.make_inputs(w)
+    mask = w.mask_kinds[0]
+    causal = bool(mask & W.MASK_CAUSAL)
+    seq = x.seqlens if (mask & W.MASK_KEY_PADDING) else None
+    extra = torch.tensor([0, 1, 127, 128, w.N - 1])
+    rows = torch.cat([x.rows, extra.expand(w.B, w.H, -1)], dim=2)
+    print(f"[case] {name}: running ({rows.shape[-1]} rows per head checked)", flush=True)
+    res = check_case(x.q, x.k, x.v, scale=x.scale, causal=causal, seqlens=seq,
+                     out_dtype=w.out_dtypes[0], rows=rows, label=name)
+    _report(name, res)
+    sys.stdout.flush()
