@@ -33,7 +33,7 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4k–128k, d=64/128, 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.txt")
-KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_f32.h", "fa_sched.h"]
+KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h"]
 
 
 def kernel_source_hash() -> str:

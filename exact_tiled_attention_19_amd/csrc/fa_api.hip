@@ -8,13 +8,13 @@
 
 #include "../../include/fa.h"
 #include "fa_fwd_bf16.h"
+#include "fa_fwd_bf16_pipe.h"
 #include "fa_fwd_f32.h"
 
 namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kBM = 128;       // query rows per workgroup (all kernels)
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -26,33 +26,43 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 using Kernel = void (*)(fa::FwdArgs);
 
-// Variant 0: the production kernel.  Variant 1: the same kernel gathering the V^T operand
-// with 16-bit LDS reads instead of LDS transpose reads.
-constexpr int kNumVariants = 2;
+struct Launch {
+    Kernel kern;
+    int bm;  // query rows per workgroup
+};
+
+// Kernel variants, all computing the same function and passing the same tests:
+//   0  software-pipelined kernel (direct-to-LDS loads, MFMA/VALU overlap)   -- production
+//   1  straightforward double-buffered kernel, LDS transpose reads of V
+//   2  the same with V^T gathered by 16-bit LDS reads
+constexpr int kNumVariants = 3;
 
 template <int D, bool CAUSAL, bool PAD, bool OUTF32>
-Kernel pick_bf16_vt(int variant) {
-    return variant == 0 ? fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>
-                        : fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>;
+Launch pick_bf16_variant(int variant) {
+    switch (variant) {
+        case 0: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32>, 128};
+        case 1: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>, 128};
+        default: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>, 128};
+    }
 }
 
 template <int D, bool OUTF32>
-Kernel pick_bf16_mask(int mask, int variant) {
+Launch pick_bf16_mask(int mask, int variant) {
     switch (mask) {
-        case 0: return pick_bf16_vt<D, false, false, OUTF32>(variant);
-        case 1: return pick_bf16_vt<D, true, false, OUTF32>(variant);
-        case 2: return pick_bf16_vt<D, false, true, OUTF32>(variant);
-        default: return pick_bf16_vt<D, true, true, OUTF32>(variant);
+        case 0: return pick_bf16_variant<D, false, false, OUTF32>(variant);
+        case 1: return pick_bf16_variant<D, true, false, OUTF32>(variant);
+        case 2: return pick_bf16_variant<D, false, true, OUTF32>(variant);
+        default: return pick_bf16_variant<D, true, true, OUTF32>(variant);
     }
 }
 
 template <int D>
-Kernel pick_f32_mask(int mask) {
+Launch pick_f32_mask(int mask) {
     switch (mask) {
-        case 0: return fa::fa_fwd_f32_kernel<D, false, false>;
-        case 1: return fa::fa_fwd_f32_kernel<D, true, false>;
-        case 2: return fa::fa_fwd_f32_kernel<D, false, true>;
-        default: return fa::fa_fwd_f32_kernel<D, true, true>;
+        case 0: return {fa::fa_fwd_f32_kernel<D, false, false>, 128};
+        case 1: return {fa::fa_fwd_f32_kernel<D, true, false>, 128};
+        case 2: return {fa::fa_fwd_f32_kernel<D, false, true>, 128};
+        default: return {fa::fa_fwd_f32_kernel<D, true, true>, 128};
     }
 }
 
@@ -76,10 +86,22 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return FA_ERR_INVALID_ARG;
     if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
     if ((mask_kind & FA_MASK_KEY_PADDING) && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
-    // sizes: element offsets are 64-bit in the kernels; workgroup counts must fit in int
-    const int64_t n_qtiles = (static_cast<int64_t>(N) + kBM - 1) / kBM;
+    // ---- kernel selection ----
+    Launch L;
+    if (in_dtype == FA_DTYPE_BF16) {
+        const bool of32 = out_dtype == FA_DTYPE_F32;
+        if (d == 64) L = of32 ? pick_bf16_mask<64, true>(mask_kind, variant) : pick_bf16_mask<64, false>(mask_kind, variant);
+        else L = of32 ? pick_bf16_mask<128, true>(mask_kind, variant) : pick_bf16_mask<128, false>(mask_kind, variant);
+    } else {
+        L = d == 64 ? pick_f32_mask<64>(mask_kind) : pick_f32_mask<128>(mask_kind);
+    }
+
+    // sizes: element offsets are 64-bit in the kernels; workgroup counts and per-head byte
+    // sizes (buffer resources) must fit in 32 bits
+    const int64_t n_qtiles = (static_cast<int64_t>(N) + L.bm - 1) / L.bm;
     const int64_t total = static_cast<int64_t>(B) * H * n_qtiles;
     if (total > 0x7fffffff || static_cast<int64_t>(B) * H > 0x7fffffff) return FA_ERR_INVALID_ARG;
+    if (static_cast<int64_t>(N) * d * 4 > 0x7fffffff) return FA_ERR_INVALID_ARG;
     const size_t in_bytes = static_cast<size_t>(B) * H * N * d * (in_dtype == FA_DTYPE_F32 ? 4 : 2);
     const size_t out_bytes = static_cast<size_t>(B) * H * N * d * (out_dtype == FA_DTYPE_F32 ? 4 : 2);
     if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) ||
@@ -90,17 +112,6 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
                 overlaps(lse, static_cast<size_t>(B) * H * N * 4, k, in_bytes) ||
                 overlaps(lse, static_cast<size_t>(B) * H * N * 4, v, in_bytes)))
         return FA_ERR_INVALID_ARG;
-
-    // ---- kernel selection ----
-    const int mask = mask_kind;
-    Kernel kern = nullptr;
-    if (in_dtype == FA_DTYPE_BF16) {
-        const bool of32 = out_dtype == FA_DTYPE_F32;
-        if (d == 64) kern = of32 ? pick_bf16_mask<64, true>(mask, variant) : pick_bf16_mask<64, false>(mask, variant);
-        else kern = of32 ? pick_bf16_mask<128, true>(mask, variant) : pick_bf16_mask<128, false>(mask, variant);
-    } else {
-        kern = d == 64 ? pick_f32_mask<64>(mask) : pick_f32_mask<128>(mask);
-    }
 
     fa::FwdArgs args;
     args.q = q;
@@ -117,7 +128,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     args.scale = scale;
     args.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
 
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(total)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(L.kern, dim3(static_cast<unsigned>(total)), dim3(kThreads), 0,
                        static_cast<hipStream_t>(stream), args);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {

@@ -1,0 +1,566 @@
+// Software-pipelined fused exact-attention forward for bf16 inputs on gfx950 (MI355X).
+//
+// Same mathematics as fa_fwd_bf16_kernel: for every query row the keys are consumed one tile
+// at a time with a running maximum, a running sum of shifted exponentials and an unnormalised
+// accumulator that are rescaled when the maximum moves ("FlashAttention Interview Questions:
+// IO Complexity, Tiling, and Numerical Stability", section "How can softmax be computed across
+// tiles?"), with S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 so every per-row
+// statistic stays inside one lane (plus one exchange with lane^32).  What changes is how the
+// work is arranged on the chip:
+//
+//   * One workgroup of four wave64s per (batch, head, BM-row query tile); each wave owns RB
+//     blocks of 32 query rows.  With RB = 2 a wave holds 64 rows and runs alone on its SIMD
+//     with up to 512 VGPRs; every K or V fragment read from LDS then feeds two MFMAs.
+//   * Pipeline.  Iteration j has two phases.  Phase A issues the MFMAs of
+//     S_{j+1}^T = K_{j+1} Q^T while the vector ALUs exponentiate the already shifted scores of
+//     tile j, sum them and pack P_j to bf16.  Phase B issues O^T += V_j^T P_j^T while the
+//     vector ALUs prepare tile j+1 (mask, row maximum, shift update, s*c - m).  P is produced
+//     and consumed inside one iteration, so only the scores are double-buffered.  In the steady
+//     state the body is one basic block and sched_group_barrier interleaves LDS reads, MFMAs
+//     and vector instructions.
+//   * Lazy rescaling.  The exponent shift is raised only when some row's tile maximum exceeds
+//     it by more than 8 (log2 units): probabilities stay below 2^8 and the accumulator rescale
+//     is skipped on almost every tile.  Numerator and denominator share the shift, so the
+//     result is unchanged.
+//   * Direct-to-LDS loads.  K/V tiles move global -> LDS with buffer_load_dwordx4 ... lds.
+//     Each instruction fills 1 KiB of LDS in lane order, so the bank-conflict-free layout is an
+//     XOR swizzle of the 16-byte chunks of each row, realised by choosing which global chunk
+//     each lane fetches.  Rows at or past N fall outside the buffer and read as zeros.
+//   * Buffers.  K_{j+2} and V_{j+1} are loaded during iteration j into the buffers whose
+//     contents (K_j, V_{j-1}) were last read in iteration j-1; one barrier per iteration.
+#pragma once
+
+#include <type_traits>
+
+#include "fa_fwd_bf16.h"
+
+namespace fa {
+
+// XOR swizzles of the 16-byte chunk index within a K or V row (row = key index in the tile).
+// K is read as 32 rows x one chunk per MFMA operand, V as 4 rows x 64 bytes per transpose
+// read; these spread both patterns over all LDS banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+    return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row) {
+    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+// 16 bytes per lane from a buffer resource straight into LDS (buffer_load_dwordx4 ... lds):
+// lane i's data lands at lds + 16 i.  A device function, not a lambda, because the builtin
+// exists only for the device.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32>
+__global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
+    constexpr int WR = 32 * RB;             // query rows per wave
+    constexpr int BM = 4 * WR;              // query rows per workgroup
+    constexpr int KC = D / 16;              // k-steps of the S MFMA
+    constexpr int NKB = BN / 32;            // 32-key blocks per tile
+    constexpr int NDB = D / 32;             // 32-wide output blocks
+    constexpr int PC = BN / 16;             // k-steps of the PV MFMA
+    constexpr int ROWB = D * 2;             // bytes per K/V row in LDS (no padding)
+    constexpr int TILEB = BN * ROWB;        // bytes per K or V tile
+    constexpr int CPR = D / 8;              // 16-byte chunks per row
+    constexpr int LPW = TILEB / 1024 / 4;   // direct-to-LDS instructions per wave per tile
+    constexpr bool PRECISE = OUT_F32;
+    // Lazy-rescale threshold (log2 units).  With a bf16 output the probabilities enter the PV
+    // product as single bf16 values, so the shift tracks the exact row maximum (threshold 0:
+    // the largest probability is then exactly 1 and carries no rounding); with the two-term
+    // split used for fp32 output a shift lagging by up to 8 costs nothing.
+    constexpr float kTau = PRECISE ? 8.0f : 0.0f;
+    static_assert(LPW >= 1 && LPW * 4 * 1024 == TILEB, "tile must split into 1 KiB pieces");
+
+    // Four separate LDS objects (not offsets into one array): the compiler must wait for an
+    // outstanding global->LDS load before any LDS read it cannot prove disjoint from it, and
+    // distinct objects are what lets it prove that.
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[TILEB];
+    constexpr int KB0 = 0, KB1 = 1, VB0 = 2, VB1 = 3;
+    auto buf = [&](int id) __attribute__((always_inline)) -> unsigned char* {
+        return id == KB0 ? kbuf0 : id == KB1 ? kbuf1 : id == VB0 ? vbuf0 : vbuf1;
+    };
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const TileCoord tc = tile_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
+    const int b = tc.bh / a.H;
+    const int N = a.N;
+    const int q0 = tc.qt * BM;
+    const int qw0 = q0 + wave * WR;          // first query row of this wave
+    int qrow[RB];                            // the rows this lane's statistics belong to
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) qrow[rb] = qw0 + 32 * rb + l32;
+    const int64_t base = (int64_t)tc.bh * N * D;
+
+    int Lk = N;
+    if (PAD) {
+        const int s = a.seqlens[b];
+        Lk = s < 0 ? 0 : (s > N ? N : s);
+    }
+    if (Lk == 0) {  // every key masked: O = 0, LSE = -inf
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            if (qrow[rb] >= N) continue;
+            if (hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow[rb]] = kNegInf;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d0 = 32 * db + 8 * j + 4 * hh;
+                    if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * D + d0) = u32x2{0u, 0u};
+                }
+        }
+        return;
+    }
+
+    int kv_end = Lk;
+    if (CAUSAL) kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
+    const int n_tiles = (kv_end + BN - 1) / BN;
+    // tiles this wave computes: under the causal mask the last tiles may lie entirely above
+    // this wave's rows and carry no visible key for any of them
+    int n_w = n_tiles;
+    if (CAUSAL) {
+        const int lim = (qw0 + WR - 1) / BN + 1;
+        n_w = lim < n_w ? lim : n_w;
+    }
+    // tiles [0, n_plain) need no mask for any row of this wave
+    int n_plain = Lk / BN;
+    if (CAUSAL) {
+        const int c = (qw0 + 1) / BN;           // tiles whose last key <= the wave's first row
+        n_plain = c < n_plain ? c : n_plain;
+    }
+
+    // Q^T operand fragments (B operand of the S MFMA), kept in VGPRs for the whole kernel
+    bf16x8 qf[RB][KC];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow[rb] < N ? qrow[rb] : N - 1) * D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            qf[rb][c] = *(const bf16x8*)(qp + 16 * c);
+            if (qrow[rb] >= N) qf[rb][c] = bf16x8{};
+        }
+    }
+
+    // ---- direct-to-LDS tile loads ---------------------------------------------------------
+    // Piece r (1 KiB) of a tile holds rows 4r .. 4r+3 (D = 128) or 8r .. 8r+7 (D = 64).  Lane
+    // lam writes physical chunk p = 64 r + lam, i.e. row p / CPR, chunk p % CPR, and fetches the
+    // logical chunk that the swizzle maps there.
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)a.k + base), (short)0, N * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const uint16_t*)a.v + base), (short)0, N * ROWB, 0x00020000);
+    uint32_t koff[LPW], voff[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int p = (i * 4 + wave) * 64 + lane;
+        const int row = p / CPR;
+        const int pch = p % CPR;
+        koff[i] = row * ROWB + (pch ^ swz_k<D>(row)) * 16;
+        voff[i] = row * ROWB + (pch ^ swz_v<D>(row)) * 16;
+    }
+    auto load_tile = [&](auto is_v, int tile, int buf_off) __attribute__((always_inline)) {
+        constexpr bool IS_V = decltype(is_v)::value;
+        const uint32_t t0 = (uint32_t)tile * (uint32_t)TILEB;
+#pragma unroll
+        for (int i = 0; i < LPW; ++i)
+            buffer_load_lds16(IS_V ? vrs : krs, buf(buf_off) + (i * 4 + wave) * 1024,
+                              (IS_V ? voff[i] : koff[i]) + t0);
+    };
+
+    // ---- LDS read addresses (bytes within a tile buffer) -----------------------------------
+    // K operand of k-step c, block kb: row 32kb + l32, logical chunk 2c + hh.
+    const int krow_base = l32 * ROWB;
+    const int kswz = swz_k<D>(l32) * 16;      // 32kb + l32 has the same swizzle as l32
+    // V^T operand (transpose read) of chunk pc, block db: row 16pc + 4hh + (l32 & 15) / 4 (+8),
+    // logical column 32db + (l32 & 16) + 4 (l32 & 3) -> chunk 4db + ((l32 & 16) >> 3) +
+    // ((l32 & 3) >> 1), byte (l32 & 1) * 8 within the chunk.
+    const int vrow = 4 * hh + ((l32 & 15) >> 2);
+    const int vswz = swz_v<D>(vrow);
+    const int vcl = ((l32 & 16) >> 3) + ((l32 & 3) >> 1);
+    int vaddr[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) vaddr[db] = vrow * ROWB + (((4 * db + vcl) ^ vswz) * 16) + (l32 & 1) * 8;
+
+    auto compute_s = [&](f32x16 (&s)[RB][NKB], int kbuf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) s[rb][kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            const int off = krow_base + (((2 * c + hh) * 16) ^ kswz);
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const bf16x8 kf = *(const bf16x8*)(buf(kbuf) + off + kb * 32 * ROWB);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][c], s[rb][kb], 0, 0, 0);
+            }
+        }
+    };
+
+    float m_run[RB], l_run[RB], alpha_pend[RB];
+    f32x16 acc[RB][NDB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        m_run[rb] = kNegInf;     // exponent shift (log2 units), raised lazily
+        l_run[rb] = 0.f;         // this lane half's running sum of 2^(scaled score - m_run)
+        alpha_pend[rb] = 1.f;    // factor the accumulator owes before the next PV product
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16{};
+    }
+    bool rescale_pend = false;
+
+    // Phase B vector work for tile `tile`: mask (edge tiles only), row maximum, lazy shift
+    // update, then the shifted scores t = s * scale * log2(e) - m in place.
+    auto prep = [&](f32x16 (&s)[RB][NKB], int tile, bool masked) __attribute__((always_inline)) {
+        const int kv0 = tile * BN;
+        if (masked) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const bool ok = key < Lk && (!CAUSAL || key <= qrow[rb]);
+                        s[rb][kb][r] = ok ? s[rb][kb][r] : kNegInf;
+                    }
+        }
+        float m_tile[RB];
+        bool need[RB];
+        bool need_any = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            float mx = s[rb][0][0];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+            mx = xor32_max(mx);
+            m_tile[rb] = (mx == kNegInf) ? kNegInf : mx * a.scale_log2;
+            need[rb] = m_tile[rb] > m_run[rb] + kTau;     // per row: the update depends on
+            need_any = need_any || need[rb];              // this row's scores only
+        }
+        const bool any = __builtin_amdgcn_ballot_w64(need_any) != 0;   // wave-uniform
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float m_new = need[rb] ? m_tile[rb] : m_run[rb];
+            const float alpha = (m_new == m_run[rb]) ? 1.f : fast_exp2(m_run[rb] - m_new);
+            m_run[rb] = m_new;
+            l_run[rb] *= alpha;          // l holds tiles < tile, all in the old shift
+            alpha_pend[rb] = alpha;      // acc still receives P V of the previous tile first
+            const float nm = (m_new == kNegInf) ? 0.f : -m_new;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float t = fmaf(s[rb][kb][r], a.scale_log2, nm);
+                    // hidden keys stay -inf (their weight is exactly 0), also when scale == 0
+                    s[rb][kb][r] = (masked && s[rb][kb][r] == kNegInf) ? kNegInf : t;
+                }
+        }
+        rescale_pend = any;
+    };
+
+    auto rescale_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha_pend[rb];
+    };
+
+    // Scheduling patterns for a block holding only a PV or only an S product: issue each
+    // MFMA's LDS operand reads just before it instead of hoisting every read to the top of
+    // the block (which would keep all operands live at once).
+    constexpr int NSF = KC * NKB;                       // K fragments per tile
+    constexpr int NPF = PC * NDB;                       // V fragments per tile
+    // Scheduling patterns: each fragment's LDS reads are issued one fragment ahead of the
+    // MFMAs that use them, so their latency is covered by the previous MFMA instead of being
+    // waited for, and reads are not all hoisted to the top of the block (which would keep
+    // every operand live at once).  VS / VP vector instructions ride along with each MFMA.
+    auto pattern_s = [](auto vs_c) __attribute__((always_inline)) {
+        constexpr int VS = decltype(vs_c)::value;
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int i = 0; i < NSF - 1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+            for (int m = 0; m < RB; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if constexpr (VS > 0) __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < RB; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if constexpr (VS > 0) __builtin_amdgcn_sched_group_barrier(0x002, VS, 0);
+        }
+    };
+    using V0 = std::integral_constant<int, 0>;
+
+    f32x16 sA[RB][NKB], sB[RB][NKB];
+    u32x4 ph[RB][PC], pl[RB][PC];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) pl[rb][pc] = u32x4{};
+
+    auto wait_loads = []() __attribute__((always_inline)) { __builtin_amdgcn_s_waitcnt(0x0F70); };  // vmcnt(0)
+
+    // ---- steady-state iteration, written in issue order -----------------------------------
+    // The iteration is a fixed sequence of slots.  A phase-A slot reads the next K fragment
+    // from LDS, issues the S MFMA(s) of the current one and a fixed slice of tile j's
+    // exponentials / sums / packing; a phase-B slot does the same with V fragments, the PV
+    // MFMA(s) and a slice of tile j+1's preparation.  sched_barrier(0) between slots keeps the
+    // compiler from regrouping them, so every MFMA has vector work beside it and every LDS
+    // read has one MFMA of time before its data is needed.
+    constexpr int NE = 16 * NKB;            // scores per lane per tile (and row block)
+    constexpr int EA = NE / NSF;            // elements exponentiated per phase-A slot
+    constexpr int HB = NPF / 2;             // phase-B slots spent on the row maximum
+    constexpr int EM = NE / HB;             // elements folded into the maximum per slot
+    constexpr int NFMA = NPF - HB - 1;      // phase-B slots left for s*c - m
+    static_assert(EA * NSF == NE && EM * HB == NE && EA % 2 == 0, "slot split");
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    auto kfrag = [&](int kbuf, int i) __attribute__((always_inline)) -> bf16x8 {
+        const int c = i / NKB, kb = i % NKB;
+        return *(const bf16x8*)(buf(kbuf) + krow_base + (((2 * c + hh) * 16) ^ kswz) + kb * 32 * ROWB);
+    };
+    auto vfrag = [&](int vbuf, int i) __attribute__((always_inline)) -> bf16x8 {
+        const int pc = i / NDB, db = i % NDB;
+        const unsigned char* p0 = buf(vbuf) + vaddr[db] + pc * 16 * ROWB;
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB)));
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    auto fast_body = [&](auto par_c, auto masked_c, int j) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr bool MASKED = decltype(masked_c)::value;
+        f32x16 (&s_cur)[RB][NKB] = PAR == 0 ? sA : sB;
+        f32x16 (&s_nxt)[RB][NKB] = PAR == 0 ? sB : sA;
+        constexpr int KB_THIS = PAR == 0 ? KB0 : KB1, KB_OTHER = PAR == 0 ? KB1 : KB0;
+        constexpr int VB_THIS = PAR == 0 ? VB0 : VB1, VB_OTHER = PAR == 0 ? VB1 : VB0;
+        const uint32_t tk = (uint32_t)(j + 2) * (uint32_t)TILEB;
+        const uint32_t tv = (uint32_t)(j + 1) * (uint32_t)TILEB;
+        int vis[RB];   // masked tiles: keys of tile j+1 at offset < vis are visible to the row
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            int lim = Lk;
+            if (CAUSAL) lim = lim < qrow[rb] + 1 ? lim : qrow[rb] + 1;
+            vis[rb] = lim - (j + 1) * BN - 4 * hh;
+        }
+        float rs[RB][2];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) rs[rb][0] = rs[rb][1] = 0.f;
+        // phase A
+        bf16x8 kf = kfrag(KB_OTHER, 0);
+#pragma unroll
+        for (int i = 0; i < NSF; ++i) {
+            if (i < LPW) buffer_load_lds16(krs, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i] + tk);
+            else if (i < 2 * LPW) buffer_load_lds16(vrs, buf(VB_OTHER) + ((i - LPW) * 4 + wave) * 1024, voff[i - LPW] + tv);
+            bf16x8 kf_next = kf;
+            if (i + 1 < NSF) kf_next = kfrag(KB_OTHER, i + 1);
+            const int c = i / NKB, kb = i % NKB;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                s_nxt[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][c], c == 0 ? f32x16{} : s_nxt[rb][kb], 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < EA; e += 2) {
+                    const int f = i * EA + e, fk = f / 16, fr = f % 16;
+                    const float p0 = fast_exp2(s_cur[rb][fk][fr]);
+                    const float p1 = fast_exp2(s_cur[rb][fk][fr + 1]);
+                    s_cur[rb][fk][fr] = p0;
+                    s_cur[rb][fk][fr + 1] = p1;
+                    rs[rb][(e / 2) & 1] += p0 + p1;
+                    const int pc = f / 8, w = (f % 8) / 2;
+                    ph[rb][pc][w] = pack_bf16x2(p0, p1);
+                    if constexpr (PRECISE)
+                        pl[rb][pc][w] = pack_bf16x2(p0 - bf16_lo_to_f32(ph[rb][pc][w]), p1 - bf16_hi_to_f32(ph[rb][pc][w]));
+                }
+            kf = kf_next;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
+        // phase B
+        float mx[RB][2];
+        bf16x8 vf = vfrag(VB_THIS, 0);
+#pragma unroll
+        for (int i = 0; i < NPF; ++i) {
+            bf16x8 vf_next = vf;
+            if (i + 1 < NPF) vf_next = vfrag(VB_THIS, i + 1);
+            const int pc = i / NDB, db = i % NDB;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, ph[rb][pc]), acc[rb][db], 0, 0, 0);
+                if constexpr (PRECISE)
+                    acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pl[rb][pc]), acc[rb][db], 0, 0, 0);
+            }
+            if (i < HB) {
+                // fold EM scores of tile j+1 into two running maxima (masked tiles: hidden keys
+                // first become -inf; key 32kb + 8(r/4) + 4hh + r%4 of the tile is visible to
+                // this lane's row iff its offset is below vis[rb] - 4hh)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < EM; e += 2) {
+                        const int f = i * EM + e, fk = f / 16, fr = f % 16;
+                        const int h = (e / 2) & 1;
+                        if constexpr (MASKED) {
+#pragma unroll
+                            for (int u = 0; u < 2; ++u) {
+                                const int off = 32 * fk + 8 * ((fr + u) >> 2) + ((fr + u) & 3);
+                                s_nxt[rb][fk][fr + u] = off < vis[rb] ? s_nxt[rb][fk][fr + u] : kNegInf;
+                            }
+                        }
+                        const float a0 = s_nxt[rb][fk][fr], a1 = s_nxt[rb][fk][fr + 1];
+                        mx[rb][h] = (i == 0 && e < 4) ? fmaxf(a0, a1) : fmaxf(mx[rb][h], fmaxf(a0, a1));
+                    }
+            } else if (i == HB) {
+                bool need[RB];
+                bool need_any = false;
+                float m_tile[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float m = xor32_max(fmaxf(mx[rb][0], mx[rb][1]));
+                    m_tile[rb] = m * a.scale_log2;
+                    need[rb] = m_tile[rb] > m_run[rb] + kTau;
+                    need_any = need_any || need[rb];
+                }
+                rescale_pend = __builtin_amdgcn_ballot_w64(need_any) != 0;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float m_new = need[rb] ? m_tile[rb] : m_run[rb];
+                    const float alpha = need[rb] ? fast_exp2(m_run[rb] - m_new) : 1.f;
+                    m_run[rb] = m_new;
+                    l_run[rb] *= alpha;
+                    alpha_pend[rb] = alpha;
+                    mx[rb][0] = -m_new;      // reuse: the shift for the fma slots
+                }
+            } else {
+                constexpr int E = (NE + NFMA - 1) / NFMA;
+                const int k0 = (i - HB - 1) * E;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int f = k0 + e;
+                        if (f < NE) {
+                            float t = fmaf(s_nxt[rb][f / 16][f % 16], a.scale_log2, mx[rb][0]);
+                            if constexpr (MASKED) t = (s_nxt[rb][f / 16][f % 16] == kNegInf) ? kNegInf : t;
+                            s_nxt[rb][f / 16][f % 16] = t;
+                        }
+                    }
+            }
+            vf = vf_next;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // One pipeline iteration for tile j (parity PAR = j & 1); on entry the score registers of
+    // parity PAR hold the shifted scores of tile j.
+    //   loads    K_{j+2} -> K buffer PAR, V_{j+1} -> V buffer !PAR (tiles past N read zeros)
+    //   phase A  MFMA S_{j+1} (K buffer !PAR)           || VALU exp / sum / pack of tile j
+    //   phase B  MFMA O^T += V_j^T P_j^T (V buffer PAR) || VALU prep of tile j+1
+    // MASKED applies the key mask to tile j+1; a tile with no visible key for a row leaves that
+    // row's statistics untouched and contributes zero probability.  A wave whose rows see no key
+    // of tile j (causal) only helps with the loads and the barrier.
+    auto step = [&](auto par_c, auto masked_c, int j) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr int KB_THIS = PAR == 0 ? KB0 : KB1;
+        constexpr int VB_OTHER = PAR == 0 ? VB1 : VB0;
+        if (rescale_pend) {
+            rescale_acc();
+            rescale_pend = false;
+        }
+        if (j < n_w) {
+            fast_body(par_c, masked_c, j);
+        } else {
+            load_tile(std::false_type{}, j + 2, KB_THIS);
+            load_tile(std::true_type{}, j + 1, VB_OTHER);
+        }
+        wait_loads();
+        __syncthreads();
+    };
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    using Mk = std::true_type;
+    using Pl = std::false_type;
+
+    // prologue: K_0, K_1, V_0 into their buffers; S_0 and its preparation
+    load_tile(std::false_type{}, 0, KB0);
+    load_tile(std::false_type{}, 1, KB1);
+    load_tile(std::true_type{}, 0, VB0);
+    wait_loads();
+    __syncthreads();
+    if (n_w > 0) {
+        compute_s(sA, KB0);
+        pattern_s(V0{});
+        prep(sA, 0, 0 >= n_plain);
+    }
+    __syncthreads();   // K buffer 0 is refilled in iteration 0
+
+    // iterations j < jm see an unmasked tile j+1; the rest apply the mask
+    int jm = n_plain - 1;
+    jm = jm < n_tiles ? jm : n_tiles;
+    int j = 0;
+    for (; j + 2 <= jm; j += 2) {
+        step(P0{}, Pl{}, j);
+        step(P1{}, Pl{}, j + 1);
+    }
+    if (j < jm) {
+        step(P0{}, Pl{}, j);
+        ++j;
+    }
+    if ((j & 1) && j < n_tiles) {
+        step(P1{}, Mk{}, j);
+        ++j;
+    }
+    for (; j + 2 <= n_tiles; j += 2) {
+        step(P0{}, Mk{}, j);
+        step(P1{}, Mk{}, j + 1);
+    }
+    if (j < n_tiles) step(P0{}, Mk{}, j);
+
+    // epilogue.  Output register r of block db is O[qrow][32db + 8(r/4) + 4hh + r%4].
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = xor32_sum(l_run[rb]);
+        const float inv_l = 1.0f / l_tot;
+        if (qrow[rb] >= N) continue;
+        if (hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow[rb]] = (m_run[rb] + __log2f(l_tot)) * kLn2;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int d0 = 32 * db + 8 * jj + 4 * hh;
+                const float o0 = acc[rb][db][4 * jj + 0] * inv_l;
+                const float o1 = acc[rb][db][4 * jj + 1] * inv_l;
+                const float o2 = acc[rb][db][4 * jj + 2] * inv_l;
+                const float o3 = acc[rb][db][4 * jj + 3] * inv_l;
+                if (OUT_F32) {
+                    *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * D + d0) = f32x4{o0, o1, o2, o3};
+                } else {
+                    *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * D + d0) =
+                        u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+                }
+            }
+    }
+}
+
+}  // namespace fa

@@ -163,3 +163,10 @@ def test_sched_mapping_is_bijective(tmp_path):
     subprocess.run(["g++", "-std=c++17", "-O1", "-I", inc, str(src), "-o", str(exe)], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
+
+
+def test_no_undefined_kernel_symbols():
+    """Every kernel the dispatcher can launch has its host stub in the library (a kernel whose
+    host-side instantiation is dropped shows up as an undefined symbol and breaks loading)."""
+    out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    assert not [l for l in out.splitlines() if "fa_fwd" in l or "_ZN2fa" in l], out

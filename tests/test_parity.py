@@ -53,7 +53,7 @@ def test_sweep_bf16(N, d, mask):
                                   out_dtype=out_dtype, label=label))
 
 
-@pytest.mark.parametrize("variant", range(1, 2))
+@pytest.mark.parametrize("variant", range(1, 3))
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_variants_bf16(variant, d, mask):
