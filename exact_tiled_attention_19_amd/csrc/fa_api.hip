@@ -28,7 +28,8 @@ using Kernel = void (*)(fa::FwdArgs);
 
 struct Launch {
     Kernel kern;
-    int bm;  // query rows per workgroup
+    int bm;       // query rows per tile
+    bool paired;  // causal tiles are processed in pairs (one work item = tiles t and n-1-t)
 };
 
 // Kernel variants, all computing the same function and passing the same tests:
@@ -40,9 +41,9 @@ constexpr int kNumVariants = 3;
 template <int D, bool CAUSAL, bool PAD, bool OUTF32>
 Launch pick_bf16_variant(int variant) {
     switch (variant) {
-        case 0: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32>, 128};
-        case 1: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>, 128};
-        default: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>, 128};
+        case 0: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32>, 128, true};
+        case 1: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>, 128, false};
+        default: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>, 128, false};
     }
 }
 
@@ -59,10 +60,10 @@ Launch pick_bf16_mask(int mask, int variant) {
 template <int D>
 Launch pick_f32_mask(int mask) {
     switch (mask) {
-        case 0: return {fa::fa_fwd_f32_kernel<D, false, false>, 128};
-        case 1: return {fa::fa_fwd_f32_kernel<D, true, false>, 128};
-        case 2: return {fa::fa_fwd_f32_kernel<D, false, true>, 128};
-        default: return {fa::fa_fwd_f32_kernel<D, true, true>, 128};
+        case 0: return {fa::fa_fwd_f32_kernel<D, false, false>, 128, false};
+        case 1: return {fa::fa_fwd_f32_kernel<D, true, false>, 128, false};
+        case 2: return {fa::fa_fwd_f32_kernel<D, false, true>, 128, false};
+        default: return {fa::fa_fwd_f32_kernel<D, true, true>, 128, false};
     }
 }
 
@@ -99,7 +100,9 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     // sizes: element offsets are 64-bit in the kernels; workgroup counts and per-head byte
     // sizes (buffer resources) must fit in 32 bits
     const int64_t n_qtiles = (static_cast<int64_t>(N) + L.bm - 1) / L.bm;
-    const int64_t total = static_cast<int64_t>(B) * H * n_qtiles;
+    const bool causal = (mask_kind & FA_MASK_CAUSAL) != 0;
+    const int64_t n_items = (L.paired && causal) ? (n_qtiles + 1) / 2 : n_qtiles;
+    const int64_t total = static_cast<int64_t>(B) * H * n_items;
     if (total > 0x7fffffff || static_cast<int64_t>(B) * H > 0x7fffffff) return FA_ERR_INVALID_ARG;
     if (static_cast<int64_t>(N) * d * 4 > 0x7fffffff) return FA_ERR_INVALID_ARG;
     const size_t in_bytes = static_cast<size_t>(B) * H * N * d * (in_dtype == FA_DTYPE_F32 ? 4 : 2);

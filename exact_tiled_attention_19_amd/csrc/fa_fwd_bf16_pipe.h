@@ -48,6 +48,10 @@ __device__ __forceinline__ int swz_v(int row) {
     return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// IEEE maximum without the canonicalising moves fmaxf needs (v_maximum3_f32 on gfx950).  The
+// scores reduced with it are finite or -inf, so NaN handling does not arise.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // 16 bytes per lane from a buffer resource straight into LDS (buffer_load_dwordx4 ... lds):
 // lane i's data lands at lds + 16 i.  A device function, not a lambda, because the builtin
 // exists only for the device.
@@ -55,8 +59,9 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// One query tile (BM rows of head bh) from start to finish; the kernel below runs one or two.
 template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32>
-__global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
+__device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     constexpr int WR = 32 * RB;             // query rows per wave
     constexpr int BM = 4 * WR;              // query rows per workgroup
     constexpr int KC = D / 16;              // k-steps of the S MFMA
@@ -93,7 +98,7 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     const int l32 = lane & 31;
     const int hh = lane >> 5;
 
-    const TileCoord tc = tile_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
+    const TileCoord tc{bh, qt};
     const int b = tc.bh / a.H;
     const int N = a.N;
     const int q0 = tc.qt * BM;
@@ -184,6 +189,9 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     // K operand of k-step c, block kb: row 32kb + l32, logical chunk 2c + hh.
     const int krow_base = l32 * ROWB;
     const int kswz = swz_k<D>(l32) * 16;      // 32kb + l32 has the same swizzle as l32
+    int kaddr[KC];                            // byte offset of k-step c's chunk in row l32
+#pragma unroll
+    for (int c = 0; c < KC; ++c) kaddr[c] = krow_base + (((2 * c + hh) * 16) ^ kswz);
     // V^T operand (transpose read) of chunk pc, block db: row 16pc + 4hh + (l32 & 15) / 4 (+8),
     // logical column 32db + (l32 & 16) + 4 (l32 & 3) -> chunk 4db + ((l32 & 16) >> 3) +
     // ((l32 & 3) >> 1), byte (l32 & 1) * 8 within the chunk.
@@ -194,6 +202,13 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vaddr[db] = vrow * ROWB + (((4 * db + vcl) ^ vswz) * 16) + (l32 & 1) * 8;
 
+    auto tile_rsrc = [&](const void* t, int64_t off, int tile) __attribute__((always_inline)) {
+        const int64_t start = (int64_t)tile * TILEB;            // bytes into this head
+        const int64_t left = (int64_t)N * ROWB - start;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)((const uint16_t*)t + off) + start),
+                                                 (short)0, left > 0 ? (int)left : 0, 0x00020000);
+    };
+
     auto compute_s = [&](f32x16 (&s)[RB][NKB], int kbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -201,7 +216,7 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
             for (int kb = 0; kb < NKB; ++kb) s[rb][kb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            const int off = krow_base + (((2 * c + hh) * 16) ^ kswz);
+            const int off = kaddr[c];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const bf16x8 kf = *(const bf16x8*)(buf(kbuf) + off + kb * 32 * ROWB);
@@ -249,7 +264,7 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[rb][kb][r]);
+                for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = vmax(mx, s[rb][kb][r]);
             mx = xor32_max(mx);
             m_tile[rb] = (mx == kNegInf) ? kNegInf : mx * a.scale_log2;
             need[rb] = m_tile[rb] > m_run[rb] + kTau;     // per row: the update depends on
@@ -337,7 +352,7 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     auto kfrag = [&](int kbuf, int i) __attribute__((always_inline)) -> bf16x8 {
         const int c = i / NKB, kb = i % NKB;
-        return *(const bf16x8*)(buf(kbuf) + krow_base + (((2 * c + hh) * 16) ^ kswz) + kb * 32 * ROWB);
+        return *(const bf16x8*)(buf(kbuf) + kaddr[c] + kb * 32 * ROWB);
     };
     auto vfrag = [&](int vbuf, int i) __attribute__((always_inline)) -> bf16x8 {
         const int pc = i / NDB, db = i % NDB;
@@ -353,8 +368,11 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
         f32x16 (&s_nxt)[RB][NKB] = PAR == 0 ? sB : sA;
         constexpr int KB_THIS = PAR == 0 ? KB0 : KB1, KB_OTHER = PAR == 0 ? KB1 : KB0;
         constexpr int VB_THIS = PAR == 0 ? VB0 : VB1, VB_OTHER = PAR == 0 ? VB1 : VB0;
-        const uint32_t tk = (uint32_t)(j + 2) * (uint32_t)TILEB;
-        const uint32_t tv = (uint32_t)(j + 1) * (uint32_t)TILEB;
+        // buffer resources starting at tiles j+2 (K) and j+1 (V): the tile offset goes into the
+        // scalar base address, so the per-lane offsets need no vector add; the record count
+        // shrinks accordingly and keeps rows past N reading as zeros
+        const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, base, j + 2);
+        const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, base, j + 1);
         int vis[RB];   // masked tiles: keys of tile j+1 at offset < vis are visible to the row
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
@@ -367,12 +385,13 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
         for (int rb = 0; rb < RB; ++rb) rs[rb][0] = rs[rb][1] = 0.f;
         // phase A
         bf16x8 kf = kfrag(KB_OTHER, 0);
+        bf16x8 kf1 = kfrag(KB_OTHER, 1);
 #pragma unroll
         for (int i = 0; i < NSF; ++i) {
-            if (i < LPW) buffer_load_lds16(krs, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i] + tk);
-            else if (i < 2 * LPW) buffer_load_lds16(vrs, buf(VB_OTHER) + ((i - LPW) * 4 + wave) * 1024, voff[i - LPW] + tv);
-            bf16x8 kf_next = kf;
-            if (i + 1 < NSF) kf_next = kfrag(KB_OTHER, i + 1);
+            if (i < LPW) buffer_load_lds16(krs_t, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i]);
+            else if (i < 2 * LPW) buffer_load_lds16(vrs_t, buf(VB_OTHER) + ((i - LPW) * 4 + wave) * 1024, voff[i - LPW]);
+            bf16x8 kf2 = kf1;           // operands are read two fragments ahead
+            if (i + 2 < NSF) kf2 = kfrag(KB_OTHER, i + 2);
             const int c = i / NKB, kb = i % NKB;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
@@ -392,7 +411,8 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
                     if constexpr (PRECISE)
                         pl[rb][pc][w] = pack_bf16x2(p0 - bf16_lo_to_f32(ph[rb][pc][w]), p1 - bf16_hi_to_f32(ph[rb][pc][w]));
                 }
-            kf = kf_next;
+            kf = kf1;
+            kf1 = kf2;
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -400,10 +420,11 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
         // phase B
         float mx[RB][2];
         bf16x8 vf = vfrag(VB_THIS, 0);
+        bf16x8 vf1 = vfrag(VB_THIS, 1);
 #pragma unroll
         for (int i = 0; i < NPF; ++i) {
-            bf16x8 vf_next = vf;
-            if (i + 1 < NPF) vf_next = vfrag(VB_THIS, i + 1);
+            bf16x8 vf2 = vf1;
+            if (i + 2 < NPF) vf2 = vfrag(VB_THIS, i + 2);
             const int pc = i / NDB, db = i % NDB;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -429,7 +450,7 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
                             }
                         }
                         const float a0 = s_nxt[rb][fk][fr], a1 = s_nxt[rb][fk][fr + 1];
-                        mx[rb][h] = (i == 0 && e < 4) ? fmaxf(a0, a1) : fmaxf(mx[rb][h], fmaxf(a0, a1));
+                        mx[rb][h] = (i == 0 && e < 4) ? vmax(a0, a1) : vmax(mx[rb][h], vmax(a0, a1));
                     }
             } else if (i == HB) {
                 bool need[RB];
@@ -437,7 +458,7 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
                 float m_tile[RB];
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const float m = xor32_max(fmaxf(mx[rb][0], mx[rb][1]));
+                    const float m = xor32_max(vmax(mx[rb][0], mx[rb][1]));
                     m_tile[rb] = m * a.scale_log2;
                     need[rb] = m_tile[rb] > m_run[rb] + kTau;
                     need_any = need_any || need[rb];
@@ -467,7 +488,8 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
                         }
                     }
             }
-            vf = vf_next;
+            vf = vf1;
+            vf1 = vf2;
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -491,8 +513,13 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
         if (j < n_w) {
             fast_body(par_c, masked_c, j);
         } else {
-            load_tile(std::false_type{}, j + 2, KB_THIS);
-            load_tile(std::true_type{}, j + 1, VB_OTHER);
+            const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, base, j + 2);
+            const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, base, j + 1);
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                buffer_load_lds16(krs_t, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i]);
+                buffer_load_lds16(vrs_t, buf(VB_OTHER) + (i * 4 + wave) * 1024, voff[i]);
+            }
         }
         wait_loads();
         __syncthreads();
@@ -560,6 +587,18 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
                         u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
                 }
             }
+    }
+}
+
+// Work item = one query tile, or under the causal mask a pair of tiles (t, n-1-t) with equal
+// total work, so all workgroups of a launch finish together.
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32>
+__global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
+    const TilePair tp = pair_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
+    pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32>(a, tp.bh, tp.qt0);
+    if (tp.qt1 >= 0) {
+        __syncthreads();   // the first tile's LDS buffers are reused
+        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32>(a, tp.bh, tp.qt1);
     }
 }
 

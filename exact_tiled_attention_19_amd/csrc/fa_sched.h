@@ -43,4 +43,31 @@ FA_HD inline TileCoord tile_of(int logical, int n_qtiles, bool causal) {
     return t;
 }
 
+// Pairs of query tiles per work item (causal mask): under the causal mask query tile t of a
+// head carries t+1 tile-rows of work, so tile t is paired with tile n-1-t and every work item
+// carries the same amount (n+1 tile-rows); an odd middle tile forms an item alone.  Without
+// the causal mask every tile is its own item.  Items of one head are contiguous.
+struct TilePair {
+    int bh;
+    int qt0;  // first query tile (the heavier one under the causal mask)
+    int qt1;  // second query tile, or -1
+};
+
+FA_HD inline int items_per_head(int n_qtiles, bool causal) { return causal ? (n_qtiles + 1) / 2 : n_qtiles; }
+
+FA_HD inline TilePair pair_of(int logical, int n_qtiles, bool causal) {
+    TilePair t;
+    const int per = items_per_head(n_qtiles, causal);
+    t.bh = logical / per;
+    const int it = logical - t.bh * per;
+    if (!causal) {
+        t.qt0 = it;
+        t.qt1 = -1;
+    } else {
+        t.qt0 = n_qtiles - 1 - it;
+        t.qt1 = (it == t.qt0) ? -1 : it;
+    }
+    return t;
+}
+
 }  // namespace fa

@@ -155,6 +155,16 @@ def test_sched_mapping_is_bijective(tmp_path):
         "    for (int x : seen) if (x != 1) ++bad;\n"
         "    if (causal && fa::tile_of(0, nq, true).qt != nq - 1) ++bad;\n"
         "  }\n"
+        "  // causal pairing: every (head, tile) exactly once, equal work (t+1 + n-t) per pair\n"
+        "  for (int nq = 1; nq <= 70; ++nq) for (int causal = 0; causal < 2; ++causal) {\n"
+        "    const int per = fa::items_per_head(nq, causal);\n"
+        "    std::vector<int> seen(3 * nq, 0);\n"
+        "    for (int l = 0; l < 3 * per; ++l) { fa::TilePair t = fa::pair_of(l, nq, causal);\n"
+        "      if (t.bh < 0 || t.bh >= 3 || t.qt0 < 0 || t.qt0 >= nq) { ++bad; continue; } ++seen[t.bh * nq + t.qt0];\n"
+        "      if (t.qt1 >= 0) { if (!causal || t.qt1 >= nq) ++bad; else ++seen[t.bh * nq + t.qt1];\n"
+        "        if (t.qt0 + t.qt1 != nq - 1) ++bad; } }\n"
+        "    for (int x : seen) if (x != 1) ++bad;\n"
+        "  }\n"
         '  std::printf("bad=%d\\n", bad);\n'
         "  return bad != 0;\n"
         "}\n")
