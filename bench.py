@@ -14,6 +14,8 @@ resident in device memory.  Prints one JSON line:
              workload (seed-chosen query rows of every head), scaled to TFLOP/s.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
+       python bench.py --calibrate-copy      (a plain conversion copy of known size, for scaling
+                                              the FETCH_SIZE / WRITE_SIZE counters to bytes)
 """
 
 from __future__ import annotations
@@ -32,7 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4k–128k, d=64/128, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_pipe_c2_causal_traffic.txt")
 KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h"]
 
 
@@ -97,17 +99,41 @@ def cpu_baseline(w, x, rows_per_head: int):
                       f"({frac:.4%} of the workload's counted FLOP), fp64 numpy, {dt:.1f} s wall"}
 
 
+COPY_ELEMS = 1 << 28   # 256 Mi elements: 1 GiB of fp32 read, 512 MiB of bf16 written
+
+
+def calibrate_copy(steps: int) -> int:
+    """Run a plain elementwise fp32 -> bf16 copy whose HBM traffic is known exactly
+    (4 bytes read and 2 bytes written per element, 1.5 GiB per launch, far above the L2 and the
+    256 MiB last-level cache), so a profiler's byte counters can be scaled to true bytes."""
+    import torch
+    dev = torch.device("cuda", 0)
+    src = torch.ones(COPY_ELEMS, dtype=torch.float32, device=dev)
+    dst = torch.empty(COPY_ELEMS, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "fp32->bf16 copy", "elements": COPY_ELEMS,
+                      "read_bytes": 4 * COPY_ELEMS, "write_bytes": 2 * COPY_ELEMS,
+                      "launches": steps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed launches first: the shader clock settles over the first ~100 ms")
     ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, the roofline workload)")
     ap.add_argument("--mask", type=int, default=None, help="override the workload's mask bits")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--variant", type=int, default=0)
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle rows per head for cpu_baseline")
+    ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only the known-size copy used to calibrate the byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -125,6 +151,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        return calibrate_copy(args.steps)
     fa.load_library()
     w = W.WORKLOADS[args.workload]
     mask = w.mask_kinds[0] if args.mask is None else args.mask
