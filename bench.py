@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4k–128k, d=64/128, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_pipe_c2_causal_traffic.txt")
 KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h"]
 
@@ -44,6 +45,11 @@ def kernel_source_hash() -> str:
         with open(os.path.join(ROOT, "exact_tiled_attention_19_amd", "csrc", s), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def compulsory_bytes(B, H, N, d, in_bytes, out_bytes) -> int:
+    """Q, K, V read once, O and the float32 LSE written once (the N x N scores never are)."""
+    return B * H * (3 * N * d * in_bytes + N * d * out_bytes + 4 * N)
 
 
 def counted_flops(B, H, N, d, causal) -> float:
@@ -126,7 +132,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed launches first: the shader clock settles over the first ~100 ms")
-    ap.add_argument("--workload", default="c2", help="c0..c4 (default c2, the roofline workload)")
+    ap.add_argument("--workload", default="c2",
+                    help="c0..c4 (default c2, the roofline workload), or a short-sequence HBM probe "
+                         "bw<N>d<d> with N in 128/256/512 and d in 64/128")
     ap.add_argument("--mask", type=int, default=None, help="override the workload's mask bits")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--variant", type=int, default=0)
@@ -154,7 +162,8 @@ def main() -> int:
     if args.calibrate_copy:
         return calibrate_copy(args.steps)
     fa.load_library()
-    w = W.WORKLOADS[args.workload]
+    probe = args.workload in W.PROBES
+    w = W.PROBES[args.workload] if probe else W.WORKLOADS[args.workload]
     mask = w.mask_kinds[0] if args.mask is None else args.mask
     causal = bool(mask & W.MASK_CAUSAL)
     out_dtype = w.out_dtypes[0] if args.out_dtype is None else (
@@ -195,9 +204,14 @@ def main() -> int:
 
     flops = counted_flops(w.B, w.H, w.N, w.d, causal)
     value = flops / (wall / args.steps) / 1e12
-    achieved = flops / avg_launch_s / 1e12
     fp32 = w.in_dtype == torch.float32
-    peak = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    nbytes = compulsory_bytes(w.B, w.H, w.N, w.d, 4 if fp32 else 2, 4 if out_dtype == torch.float32 else 2)
+    if probe:   # HBM-bound: compulsory bytes per launch against the HBM peak
+        bound, unit, peak, achieved = "hbm", "GB/s", PEAK_HBM_GBS, nbytes / avg_launch_s / 1e9
+    else:       # MFMA-bound: counted FLOP per launch against the dense MFMA peak of the input dtype
+        bound, unit = "mfma", "TFLOP/s"
+        peak = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+        achieved = flops / avg_launch_s / 1e12
     mask_name = {0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[mask]
     workload_id = f"{w.name}:{mask_name}:{'f32' if out_dtype == torch.float32 else 'bf16'}-out"
     traffic = recorded_traffic(workload_id)
@@ -220,13 +234,13 @@ def main() -> int:
                         f"{'fp32' if fp32 else 'bf16'} in, "
                         f"{'fp32' if out_dtype == torch.float32 else 'bf16'} out, fp32 LSE",
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name,
-            "flop_per_step": flops, "variant": args.variant,
+            "flop_per_step": flops, "compulsory_bytes_per_step": nbytes, "variant": args.variant,
         },
         "roofline": {
-            "bound": "mfma",
+            "bound": bound,
             "achieved": round(achieved, 3),
             "peak": peak,
-            "unit": "TFLOP/s",
+            "unit": unit,
             "frac": round(achieved / peak, 5),
             "traffic": traffic,
             "kernel_avg_ms": round(avg_launch_s * 1e3, 5),

@@ -356,12 +356,19 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
             const float p1 = fast_exp2(s[rb][fk][fr + 1]);
             rs[rb] += p0 + p1;
             const int pc = f / 8, w = (f % 8) / 2;
-            const uint32_t hw = pack_bf16x2(p0, p1);
+            uint32_t hw = pack_bf16x2(p0, p1);
+            // Keep the packing in this slot: its results are used only after the (rarely taken)
+            // re-base branch, and left alone the compiler sinks it there as one serial burst.
+            asm volatile("" : "+v"(hw));
             ph[rb][pc][w] = hw;
-            if constexpr (PRECISE)
-                pl[rb][pc][w] = pack_bf16x2(p0 - bf16_lo_to_f32(hw), p1 - bf16_hi_to_f32(hw));
-            else
+            if constexpr (PRECISE) {
+                uint32_t lw = pack_bf16x2(p0 - bf16_lo_to_f32(hw), p1 - bf16_hi_to_f32(hw));
+                asm volatile("" : "+v"(lw));
+                pl[rb][pc][w] = lw;
+            } else {
                 ns[rb] = add_bf16_pair(hw, ns[rb]);
+                asm volatile("" : "+v"(ns[rb]));
+            }
         }
     };
     // Rare path: some row's tile sum exceeded its limit.  Each such row whose tile maximum lies

@@ -67,6 +67,18 @@ WORKLOADS = {
 }
 
 
+# Short-sequence bandwidth probes (not among the five named workloads): non-causal heads so
+# short that the forward is bound by HBM traffic rather than by the MFMAs (arithmetic intensity
+# N/2 FLOP per byte for bf16 in and out, below the ~315 FLOP/B ridge of the chip), with B*H
+# chosen so that Q, K, V and O together take about 1 GiB.
+PROBES = {
+    f"bw{n}d{d}": Workload(f"bw{n}d{d}", (1 << 30) // (4 * n * d * 2) // 64, 64, n, d, torch.bfloat16,
+                           (torch.bfloat16,), (MASK_NONE,), seed=10, sample_rows=64,
+                           description=f"HBM-bound probe, N={n}, d={d}, Q+K+V+O = 1 GiB")
+    for n in (128, 256, 512) for d in (64, 128)
+}
+
+
 @dataclasses.dataclass
 class Inputs:
     q: torch.Tensor          # [B,H,N,d] CPU, in_dtype
