@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -138,6 +139,8 @@ def main() -> int:
     ap.add_argument("--mask", type=int, default=None, help="override the workload's mask bits")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--variant", type=int, default=0)
+    ap.add_argument("--qk-gain", type=float, default=None,
+                    help="override the workload's Q/K gain (c3 uses 3: logit std ~ 9; 1 gives flat rows)")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -169,6 +172,8 @@ def main() -> int:
     out_dtype = w.out_dtypes[0] if args.out_dtype is None else (
         torch.bfloat16 if args.out_dtype == "bf16" else torch.float32)
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    if args.qk_gain is not None:
+        w = dataclasses.replace(w, qk_gain=args.qk_gain)
     x = W.make_inputs(w, mask_kind=mask)
     dev = torch.device("cuda", 0)
     q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
@@ -230,9 +235,10 @@ def main() -> int:
         "dtype": "f32" if fp32 else "bf16",
         "data": "synthetic (seeded normal Q, K, V of the workload's shape; no dataset)",
         "config": {
-            "workload": f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {mask_name} mask, "
-                        f"{'fp32' if fp32 else 'bf16'} in, "
-                        f"{'fp32' if out_dtype == torch.float32 else 'bf16'} out, fp32 LSE",
+            "workload": (f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {mask_name} mask, "
+                         + (f"Q/K gain {w.qk_gain:g}, " if w.qk_gain != 1.0 else "")
+                         + f"{'fp32' if fp32 else 'bf16'} in, "
+                         + f"{'fp32' if out_dtype == torch.float32 else 'bf16'} out, fp32 LSE"),
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name,
             "flop_per_step": flops, "compulsory_bytes_per_step": nbytes, "variant": args.variant,
         },

@@ -1,36 +1,28 @@
 // Software-pipelined fused exact-attention forward for bf16 inputs on gfx950 (MI355X).
 //
 // Same mathematics as fa_fwd_bf16_kernel: for every query row the keys are consumed one tile
-// at a time with a running exponent shift, a running sum of shifted exponentials and an
-// unnormalised accumulator that are rescaled when the shift moves ("FlashAttention Interview
-// Questions: IO Complexity, Tiling, and Numerical Stability", section "How can softmax be
-// computed across tiles?"), with S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 so
-// every per-row statistic stays inside one lane (plus one exchange with lane^32).  What
-// changes is how the work is arranged on the chip:
+// at a time with a running maximum, a running sum of shifted exponentials and an unnormalised
+// accumulator that are rescaled when the maximum moves ("FlashAttention Interview Questions:
+// IO Complexity, Tiling, and Numerical Stability", section "How can softmax be computed across
+// tiles?"), with S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16_bf16 so every per-row
+// statistic stays inside one lane (plus one exchange with lane^32).  What changes is how the
+// work is arranged on the chip:
 //
 //   * One workgroup of four wave64s per (batch, head, 128-row query tile), 32 rows per wave,
 //     two workgroups per CU.  Under the causal mask a workgroup runs the tile pair (t, n-1-t).
 //   * Pipeline.  Iteration j has two phases.  Phase A issues the MFMAs of
-//     S_{j+1}^T = K_{j+1} Q^T while the vector ALUs exponentiate tile j's shifted scores, sum
-//     them and pack P_j to bf16.  Phase B issues O^T += V_j^T P_j^T while the vector ALUs shift
-//     tile j+1 (t = s * scale * log2(e) - m, masked keys selected to -inf).  sched_barrier
-//     between slots keeps every MFMA paired with a fixed slice of vector work.
-//   * Lagging shift, no per-tile maximum.  A tile is exponentiated against the shift left by
-//     earlier tiles.  On MI355X the vector work per score sets the pace next to the MFMAs, and
-//     a per-tile row maximum plus the accumulator rescale it triggers cost a third of it.  The
-//     shift is exact for the first tile; later it only has to keep the exponentials finite and
-//     well scaled, so a row's shift is raised only when the row's tile sum exceeds its running
-//     sum or 2^8 (the latter also catches an overflow to infinity): that row is then re-based
-//     on the exact row maximum, its accumulator and sums are rescaled and the tile is
-//     exponentiated again from the shifted scores, which are kept until the check.  Numerator
-//     and denominator share every shift, so the result is unchanged; re-basing whenever a new
-//     key outweighs everything before it keeps the dominant probability of a peaked row at
-//     exactly 1, which the bf16 rounding of P needs.
-//   * Normalisation.  With a bf16 output, P enters the PV product as single bf16 values, so the
-//     output is divided by the sum of exactly those rounded values (v_dot2c_f32_bf16 against
-//     (1, 1)): a row dominated by one key then returns that key's value row exactly, whatever
-//     the shift.  The log-sum-exp always uses the float32 sum of the unrounded exponentials.
-//     With a float32 output P = P_hi + P_lo (two bf16 products) and the float32 sum serves both.
+//     S_{j+1}^T = K_{j+1} Q^T while the vector ALUs exponentiate the already shifted scores of
+//     tile j, sum them and pack P_j to bf16.  Phase B issues O^T += V_j^T P_j^T while the vector
+//     ALUs prepare tile j+1 (mask, row maximum, shift update, s*c - m).  P is produced and
+//     consumed inside one iteration, so only the scores are double-buffered.  The iteration is
+//     written as a fixed sequence of slots, one MFMA with its LDS read and a slice of vector
+//     work each, kept in that order by sched_barrier.
+//   * Shift policy.  With a bf16 output the shift is the exact running row maximum, so the
+//     largest probability of every row is exactly 1 and carries no bf16 rounding; the
+//     accumulator is rescaled (per row, applied wave-wide) whenever some row's maximum rises.
+//     With a float32 output (P = P_hi + P_lo, two bf16 products) the shift is raised only when
+//     a row's tile maximum exceeds it by more than 8 (log2 units), which skips most rescales.
+//     Numerator and denominator share every shift, so the result is unchanged.
 //   * Direct-to-LDS loads.  K/V tiles move global -> LDS with buffer_load_dwordx4 ... lds.
 //     Each instruction fills 1 KiB of LDS in lane order, so the bank-conflict-free layout is an
 //     XOR swizzle of the 16-byte chunks of each row, realised by choosing which global chunk
@@ -61,13 +53,6 @@ __device__ __forceinline__ int swz_v(int row) {
 // scores reduced with it are finite or -inf, so NaN handling does not arise.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-// Sum of the two bf16 halves of w added to acc in float32 (v_dot2c_f32_bf16 against (1, 1)).
-__device__ __forceinline__ float add_bf16_pair(uint32_t w, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), acc,
-                                           false);
-}
-
 // 16 bytes per lane from a buffer resource straight into LDS (buffer_load_dwordx4 ... lds):
 // lane i's data lands at lds + 16 i.  A device function, not a lambda, because the builtin
 // exists only for the device.
@@ -89,9 +74,11 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     constexpr int CPR = D / 8;              // 16-byte chunks per row
     constexpr int LPW = TILEB / 1024 / 4;   // direct-to-LDS instructions per wave per tile
     constexpr bool PRECISE = OUT_F32;
-    // A row's tile sum above this means some exponential exceeds it (or overflowed): the tile is
-    // then re-based on the exact row maximum.
-    constexpr float kSumLimit = 256.0f;
+    // Shift threshold (log2 units).  With a bf16 output the probabilities enter the PV product
+    // as single bf16 values, so the shift tracks the exact row maximum (threshold 0: the largest
+    // probability is then exactly 1 and carries no rounding); with the two-term split used for
+    // a float32 output a shift lagging by up to 8 costs nothing.
+    constexpr float kTau = PRECISE ? 8.0f : 0.0f;
     static_assert(LPW >= 1 && LPW * 4 * 1024 == TILEB, "tile must split into 1 KiB pieces");
 
     // Four separate LDS objects (not offsets into one array): the compiler must wait for an
@@ -147,9 +134,13 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     int kv_end = Lk;
     if (CAUSAL) kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
     const int n_tiles = (kv_end + BN - 1) / BN;
-    // Every wave runs all n_tiles iterations.  Under the causal mask the last tile may lie
-    // entirely above a wave's rows: its scores are then all masked, its probabilities exactly 0
-    // and its PV product adds nothing (that wave would otherwise wait at the barrier).
+    // tiles this wave computes: under the causal mask the last tiles may lie entirely above
+    // this wave's rows and carry no visible key for any of them
+    int n_w = n_tiles;
+    if (CAUSAL) {
+        const int lim = (qw0 + WR - 1) / BN + 1;
+        n_w = lim < n_w ? lim : n_w;
+    }
     // tiles [0, n_plain) need no mask for any row of this wave
     int n_plain = Lk / BN;
     if (CAUSAL) {
@@ -237,21 +228,22 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
         }
     };
 
-    float m_run[RB], l_run[RB], n_run[RB], lim[RB];
+    float m_run[RB], l_run[RB], alpha_pend[RB];
     f32x16 acc[RB][NDB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        m_run[rb] = 0.f;         // exponent shift (log2 units)
-        l_run[rb] = 0.f;         // this lane half's float32 sum of 2^(scaled score - m_run)
-        n_run[rb] = 0.f;         // bf16 output: the same sum over the bf16-rounded values
-        lim[rb] = kSumLimit;     // re-base limit of the next tile sum (no running sum yet)
+        m_run[rb] = kNegInf;     // exponent shift (log2 units), raised lazily
+        l_run[rb] = 0.f;         // this lane half's running sum of 2^(scaled score - m_run)
+        alpha_pend[rb] = 1.f;    // factor the accumulator owes before the next PV product
 #pragma unroll
         for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16{};
     }
+    bool rescale_pend = false;
 
-    // First tile: mask (edge tiles only), exact row maximum as the shift, then the shifted
-    // scores t = s * scale * log2(e) - m in place (hidden keys -inf).
-    auto prep_first = [&](f32x16 (&s)[RB][NKB], bool masked) __attribute__((always_inline)) {
+    // Phase B vector work for tile `tile`: mask (edge tiles only), row maximum, lazy shift
+    // update, then the shifted scores t = s * scale * log2(e) - m in place.
+    auto prep = [&](f32x16 (&s)[RB][NKB], int tile, bool masked) __attribute__((always_inline)) {
+        const int kv0 = tile * BN;
         if (masked) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
@@ -259,11 +251,14 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                        const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
                         const bool ok = key < Lk && (!CAUSAL || key <= qrow[rb]);
                         s[rb][kb][r] = ok ? s[rb][kb][r] : kNegInf;
                     }
         }
+        float m_tile[RB];
+        bool need[RB];
+        bool need_any = false;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             float mx = s[rb][0][0];
@@ -272,27 +267,44 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
 #pragma unroll
                 for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = vmax(mx, s[rb][kb][r]);
             mx = xor32_max(mx);
-            // a row with no visible key yet keeps a finite shift of 0
-            m_run[rb] = (mx == kNegInf) ? 0.f : mx * a.scale_log2;
+            m_tile[rb] = (mx == kNegInf) ? kNegInf : mx * a.scale_log2;
+            need[rb] = m_tile[rb] > m_run[rb] + kTau;     // per row: the update depends on
+            need_any = need_any || need[rb];              // this row's scores only
+        }
+        const bool any = __builtin_amdgcn_ballot_w64(need_any) != 0;   // wave-uniform
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const float m_new = need[rb] ? m_tile[rb] : m_run[rb];
+            const float alpha = (m_new == m_run[rb]) ? 1.f : fast_exp2(m_run[rb] - m_new);
+            m_run[rb] = m_new;
+            l_run[rb] *= alpha;          // l holds tiles < tile, all in the old shift
+            alpha_pend[rb] = alpha;      // acc still receives P V of the previous tile first
+            const float nm = (m_new == kNegInf) ? 0.f : -m_new;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float t = fmaf(s[rb][kb][r], a.scale_log2, -m_run[rb]);
+                    const float t = fmaf(s[rb][kb][r], a.scale_log2, nm);
+                    // hidden keys stay -inf (their weight is exactly 0), also when scale == 0
                     s[rb][kb][r] = (masked && s[rb][kb][r] == kNegInf) ? kNegInf : t;
                 }
         }
+        rescale_pend = any;
     };
 
-    // Scheduling patterns for a block holding only a PV or only an S product: issue each
-    // MFMA's LDS operand reads just before it instead of hoisting every read to the top of
-    // the block (which would keep all operands live at once).
+    auto rescale_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha_pend[rb];
+    };
+
     constexpr int NSF = KC * NKB;                       // K fragments per tile
     constexpr int NPF = PC * NDB;                       // V fragments per tile
-    // Scheduling patterns: each fragment's LDS reads are issued one fragment ahead of the
-    // MFMAs that use them, so their latency is covered by the previous MFMA instead of being
-    // waited for, and reads are not all hoisted to the top of the block (which would keep
-    // every operand live at once).  VS / VP vector instructions ride along with each MFMA.
+    // Scheduling pattern of the prologue's S product: each fragment's LDS read is issued one
+    // fragment ahead of its MFMA, so its latency is covered by the previous MFMA and the reads
+    // are not all hoisted to the top (which would keep every operand live at once); VS vector
+    // instructions ride along with each MFMA.
     auto pattern_s = [](auto vs_c) __attribute__((always_inline)) {
         constexpr int VS = decltype(vs_c)::value;
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
@@ -331,8 +343,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     // read has one MFMA of time before its data is needed.
     constexpr int NE = 16 * NKB;            // scores per lane per tile (and row block)
     constexpr int EA = NE / NSF;            // elements exponentiated per phase-A slot
-    constexpr int EB = NE / NPF;            // elements shifted per phase-B slot
-    static_assert(EA * NSF == NE && EB * NPF == NE && EA % 2 == 0, "slot split");
+    constexpr int HB = NPF / 2;             // phase-B slots spent on the row maximum
+    constexpr int EM = NE / HB;             // elements folded into the maximum per slot
+    constexpr int NFMA = NPF - HB - 1;      // phase-B slots left for s*c - m
+    static_assert(EA * NSF == NE && EM * HB == NE && EA % 2 == 0, "slot split");
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
     auto kfrag = [&](int kbuf, int i) __attribute__((always_inline)) -> bf16x8 {
         const int c = i / NKB, kb = i % NKB;
@@ -344,64 +358,6 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
         const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0));
         const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB)));
         return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-    };
-    // Exponentials, sums and bf16 packing of elements [f0, f0 + n) of row block rb's shifted
-    // scores (kept in place for a possible re-base).
-    auto expo = [&](f32x16 (&s)[RB][NKB], int rb, int f0, int n, float (&rs)[RB], float (&ns)[RB])
-        __attribute__((always_inline)) {
-#pragma unroll
-        for (int e = 0; e < n; e += 2) {
-            const int f = f0 + e, fk = f / 16, fr = f % 16;
-            const float p0 = fast_exp2(s[rb][fk][fr]);
-            const float p1 = fast_exp2(s[rb][fk][fr + 1]);
-            rs[rb] += p0 + p1;
-            const int pc = f / 8, w = (f % 8) / 2;
-            uint32_t hw = pack_bf16x2(p0, p1);
-            // Keep the packing in this slot: its results are used only after the (rarely taken)
-            // re-base branch, and left alone the compiler sinks it there as one serial burst.
-            asm volatile("" : "+v"(hw));
-            ph[rb][pc][w] = hw;
-            if constexpr (PRECISE) {
-                uint32_t lw = pack_bf16x2(p0 - bf16_lo_to_f32(hw), p1 - bf16_hi_to_f32(hw));
-                asm volatile("" : "+v"(lw));
-                pl[rb][pc][w] = lw;
-            } else {
-                ns[rb] = add_bf16_pair(hw, ns[rb]);
-                asm volatile("" : "+v"(ns[rb]));
-            }
-        }
-    };
-    // Rare path: some row's tile sum exceeded its limit.  Each such row whose tile maximum lies
-    // above its shift takes that maximum as the new shift (the accumulator and both sums, which
-    // hold the earlier tiles only, are rescaled), and the tile is exponentiated again.
-    auto rebase = [&](f32x16 (&s)[RB][NKB], float (&rs)[RB], float (&ns)[RB], const uint64_t (&over)[RB])
-        __attribute__((always_inline)) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float mx = s[rb][0][0];
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = vmax(mx, s[rb][kb][r]);
-            mx = xor32_max(mx);
-            // only a row that is itself over the limit moves its shift; every other row recomputes
-            // exactly the values it had
-            const bool row_over = ((over[rb] >> l32) | (over[rb] >> (l32 + 32))) & 1;
-            const float rise = (row_over && mx > 0.f) ? mx : 0.f;
-            const float alpha = fast_exp2(-rise);
-            m_run[rb] += rise;
-            l_run[rb] *= alpha;
-            n_run[rb] *= alpha;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db) acc[rb][db] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[rb][kb][r] -= rise;
-            rs[rb] = 0.f;
-            ns[rb] = 0.f;
-            expo(s, rb, 0, NE, rs, ns);
-        }
     };
     auto fast_body = [&](auto par_c, auto masked_c, int j) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_c)::value;
@@ -422,9 +378,9 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
             if (CAUSAL) lim = lim < qrow[rb] + 1 ? lim : qrow[rb] + 1;
             vis[rb] = lim - (j + 1) * BN - 4 * hh;
         }
-        float rs[RB], ns[RB];
+        float rs[RB][2];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) rs[rb] = ns[rb] = 0.f;
+        for (int rb = 0; rb < RB; ++rb) rs[rb][0] = rs[rb][1] = 0.f;
         // phase A
         bf16x8 kf = kfrag(KB_OTHER, 0);
         bf16x8 kf1 = kfrag(KB_OTHER, 1);
@@ -439,30 +395,28 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
             for (int rb = 0; rb < RB; ++rb)
                 s_nxt[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][c], c == 0 ? f32x16{} : s_nxt[rb][kb], 0, 0, 0);
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) expo(s_cur, rb, i * EA, EA, rs, ns);
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < EA; e += 2) {
+                    const int f = i * EA + e, fk = f / 16, fr = f % 16;
+                    const float p0 = fast_exp2(s_cur[rb][fk][fr]);
+                    const float p1 = fast_exp2(s_cur[rb][fk][fr + 1]);
+                    s_cur[rb][fk][fr] = p0;
+                    s_cur[rb][fk][fr + 1] = p1;
+                    rs[rb][(e / 2) & 1] += p0 + p1;
+                    const int pc = f / 8, w = (f % 8) / 2;
+                    ph[rb][pc][w] = pack_bf16x2(p0, p1);
+                    if constexpr (PRECISE)
+                        pl[rb][pc][w] = pack_bf16x2(p0 - bf16_lo_to_f32(ph[rb][pc][w]), p1 - bf16_hi_to_f32(ph[rb][pc][w]));
+                }
             kf = kf1;
             kf1 = kf2;
             __builtin_amdgcn_sched_barrier(0);
         }
-        // a row re-bases when one of its lane halves' tile sum exceeds the smaller of the row's
-        // running sum and kSumLimit: a new key that outweighs everything seen so far gets the
-        // exact maximum as its shift
-        uint64_t over[RB];
-        uint64_t any = 0;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            over[rb] = __builtin_amdgcn_ballot_w64(!(rs[rb] <= lim[rb]));
-            any |= over[rb];
-        }
-        if (any != 0) rebase(s_cur, rs, ns, over);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            l_run[rb] += rs[rb];
-            n_run[rb] += ns[rb];
-            const float l_row = xor32_sum(l_run[rb]);      // needed only by the next check
-            lim[rb] = l_row < kSumLimit ? l_row : kSumLimit;
-        }
+        for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
         // phase B
+        float mx[RB][2];
         bf16x8 vf = vfrag(VB_THIS, 0);
         bf16x8 vf1 = vfrag(VB_THIS, 1);
 #pragma unroll
@@ -476,20 +430,62 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
                 if constexpr (PRECISE)
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pl[rb][pc]), acc[rb][db], 0, 0, 0);
             }
-            // shift EB scores of tile j+1 (masked tiles: key 32kb + 8(r/4) + 4hh + r%4 of the
-            // tile is visible to this lane's row iff its offset is below vis[rb] - 4hh)
+            if (i < HB) {
+                // fold EM scores of tile j+1 into two running maxima (masked tiles: hidden keys
+                // first become -inf; key 32kb + 8(r/4) + 4hh + r%4 of the tile is visible to
+                // this lane's row iff its offset is below vis[rb] - 4hh)
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-                for (int e = 0; e < EB; ++e) {
-                    const int f = i * EB + e, fk = f / 16, fr = f % 16;
-                    float t = fmaf(s_nxt[rb][fk][fr], a.scale_log2, -m_run[rb]);
-                    if constexpr (MASKED) {
-                        const int off = 32 * fk + 8 * (fr >> 2) + (fr & 3);
-                        t = off < vis[rb] ? t : kNegInf;
+                    for (int e = 0; e < EM; e += 2) {
+                        const int f = i * EM + e, fk = f / 16, fr = f % 16;
+                        const int h = (e / 2) & 1;
+                        if constexpr (MASKED) {
+#pragma unroll
+                            for (int u = 0; u < 2; ++u) {
+                                const int off = 32 * fk + 8 * ((fr + u) >> 2) + ((fr + u) & 3);
+                                s_nxt[rb][fk][fr + u] = off < vis[rb] ? s_nxt[rb][fk][fr + u] : kNegInf;
+                            }
+                        }
+                        const float a0 = s_nxt[rb][fk][fr], a1 = s_nxt[rb][fk][fr + 1];
+                        mx[rb][h] = (i == 0 && e < 4) ? vmax(a0, a1) : vmax(mx[rb][h], vmax(a0, a1));
                     }
-                    s_nxt[rb][fk][fr] = t;
+            } else if (i == HB) {
+                bool need[RB];
+                bool need_any = false;
+                float m_tile[RB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float m = xor32_max(vmax(mx[rb][0], mx[rb][1]));
+                    m_tile[rb] = m * a.scale_log2;
+                    need[rb] = m_tile[rb] > m_run[rb] + kTau;
+                    need_any = need_any || need[rb];
                 }
+                rescale_pend = __builtin_amdgcn_ballot_w64(need_any) != 0;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const float m_new = need[rb] ? m_tile[rb] : m_run[rb];
+                    const float alpha = need[rb] ? fast_exp2(m_run[rb] - m_new) : 1.f;
+                    m_run[rb] = m_new;
+                    l_run[rb] *= alpha;
+                    alpha_pend[rb] = alpha;
+                    mx[rb][0] = -m_new;      // reuse: the shift for the fma slots
+                }
+            } else {
+                constexpr int E = (NE + NFMA - 1) / NFMA;
+                const int k0 = (i - HB - 1) * E;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < E; ++e) {
+                        const int f = k0 + e;
+                        if (f < NE) {
+                            float t = fmaf(s_nxt[rb][f / 16][f % 16], a.scale_log2, mx[rb][0]);
+                            if constexpr (MASKED) t = (s_nxt[rb][f / 16][f % 16] == kNegInf) ? kNegInf : t;
+                            s_nxt[rb][f / 16][f % 16] = t;
+                        }
+                    }
+            }
             vf = vf1;
             vf1 = vf2;
             __builtin_amdgcn_sched_barrier(0);
@@ -499,13 +495,30 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     // One pipeline iteration for tile j (parity PAR = j & 1); on entry the score registers of
     // parity PAR hold the shifted scores of tile j.
     //   loads    K_{j+2} -> K buffer PAR, V_{j+1} -> V buffer !PAR (tiles past N read zeros)
-    //   phase A  MFMA S_{j+1} (K buffer !PAR)           || VALU exp / sums / pack of tile j,
-    //                                                      then the overflow check (rare re-base)
-    //   phase B  MFMA O^T += V_j^T P_j^T (V buffer PAR) || VALU shift (and mask) of tile j+1
-    // MASKED applies the key mask to tile j+1; a tile with no visible key for a row contributes
-    // zero probability and leaves that row's statistics unchanged.
+    //   phase A  MFMA S_{j+1} (K buffer !PAR)           || VALU exp / sum / pack of tile j
+    //   phase B  MFMA O^T += V_j^T P_j^T (V buffer PAR) || VALU prep of tile j+1
+    // MASKED applies the key mask to tile j+1; a tile with no visible key for a row leaves that
+    // row's statistics untouched and contributes zero probability.  A wave whose rows see no key
+    // of tile j (causal) only helps with the loads and the barrier.
     auto step = [&](auto par_c, auto masked_c, int j) __attribute__((always_inline)) {
-        fast_body(par_c, masked_c, j);
+        constexpr int PAR = decltype(par_c)::value;
+        constexpr int KB_THIS = PAR == 0 ? KB0 : KB1;
+        constexpr int VB_OTHER = PAR == 0 ? VB1 : VB0;
+        if (rescale_pend) {
+            rescale_acc();
+            rescale_pend = false;
+        }
+        if (j < n_w) {
+            fast_body(par_c, masked_c, j);
+        } else {
+            const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, base, j + 2);
+            const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, base, j + 1);
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                buffer_load_lds16(krs_t, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i]);
+                buffer_load_lds16(vrs_t, buf(VB_OTHER) + (i * 4 + wave) * 1024, voff[i]);
+            }
+        }
         wait_loads();
         __syncthreads();
     };
@@ -520,9 +533,11 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     load_tile(std::true_type{}, 0, VB0);
     wait_loads();
     __syncthreads();
-    compute_s(sA, KB0);
-    pattern_s(V0{});
-    prep_first(sA, 0 >= n_plain);
+    if (n_w > 0) {
+        compute_s(sA, KB0);
+        pattern_s(V0{});
+        prep(sA, 0, 0 >= n_plain);
+    }
     __syncthreads();   // K buffer 0 is refilled in iteration 0
 
     // iterations j < jm see an unmasked tile j+1; the rest apply the mask
@@ -551,7 +566,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = xor32_sum(l_run[rb]);
-        const float inv_l = 1.0f / (PRECISE ? l_tot : xor32_sum(n_run[rb]));
+        const float inv_l = 1.0f / l_tot;
         if (qrow[rb] >= N) continue;
         if (hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow[rb]] = (m_run[rb] + __log2f(l_tot)) * kLn2;
 #pragma unroll
