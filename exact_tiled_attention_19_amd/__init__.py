@@ -1,6 +1,6 @@
 """Fused exact-attention forward for AMD Instinct MI355X (gfx950).
 
-``forward(q, k, v, ...)`` runs the HIP kernels of ``libfa.so`` through its C ABI
+``forward(q, k, v, ...)`` and ``backward(q, k, v, o, lse, dout, ...)`` run the HIP kernels of ``libfa.so`` through its C ABI
 (include/fa.h); PyTorch only supplies device memory and the stream.
 """
 
@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     FaInvalidArgument,
     FaUnsupported,
     LIB_PATH,
+    backward,
+    fa_bwd,
     fa_fwd,
     forward,
     load_library,

@@ -37,6 +37,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "fa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP]),
     "fa_fwd_variant": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP, _I]),
+    "fa_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I,
+                    _VP]),
     "fa_variant_count": (_I, []),
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
@@ -160,6 +162,59 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
                 _ptr(seqlens), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype], stream, variant)
     _check(st)
     return out, lse
+
+
+def fa_bwd(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask_kind, seqlens, in_dtype,
+           grad_dtype, stream) -> int:
+    """Raw call of the backward pass through the C ABI (pointers as ints or None)."""
+    return load_library().fa_bwd(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, ctypes.c_float(scale),
+                                 mask_kind, seqlens, in_dtype, grad_dtype, stream)
+
+
+def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+             dout: torch.Tensor, *, scale: Optional[float] = None, causal: bool = False,
+             seqlens: Optional[torch.Tensor] = None, out: Optional[Tuple[torch.Tensor, ...]] = None,
+             delta: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Gradients (dQ, dK, dV) of the forward pass on the GPU, float32.
+
+    q, k, v: the forward inputs; o, lse: what ``forward`` returned for them (o in bfloat16);
+    dout: the gradient arriving at o.  All [B, H, N, d] contiguous bfloat16 device tensors (lse
+    float32 [B, H, N]).  scale, causal and seqlens as for ``forward``.
+    out: optional preallocated (dq, dk, dv) float32 tensors; delta: optional float32 [B, H, N]
+    workspace (allocated here when omitted).
+    """
+    ts = (q, k, v, o, dout)
+    if not all(t.is_cuda for t in ts) or not lse.is_cuda:
+        raise ValueError("all tensors must be device tensors")
+    if any(t.dtype != torch.bfloat16 for t in ts):
+        raise ValueError("q, k, v, o and dout must be bfloat16")
+    if q.dim() != 4 or any(t.shape != q.shape for t in ts):
+        raise ValueError("q, k, v, o and dout must all be [B, H, N, d]")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("q, k, v, o and dout must be contiguous")
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
+    if seqlens is not None:
+        if not seqlens.is_cuda or seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 device tensor with B entries")
+        mask |= FA_MASK_KEY_PADDING
+    if out is None:
+        out = tuple(torch.empty((B, H, N, d), dtype=torch.float32, device=q.device) for _ in range(3))
+    elif len(out) != 3 or any(t.shape != q.shape or t.dtype != torch.float32 or not t.is_contiguous() for t in out):
+        raise ValueError("out must be three contiguous float32 [B, H, N, d] tensors")
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
+        raise ValueError("delta must be a contiguous float32 [B, H, N] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(delta), _ptr(out[0]), _ptr(out[1]),
+                _ptr(out[2]), B, H, N, d, float(scale), mask, _ptr(seqlens), FA_DTYPE_BF16, FA_DTYPE_F32, stream)
+    _check(st)
+    return out
 
 
 def variant_count() -> int:

@@ -10,6 +10,7 @@
 #include "fa_fwd_bf16.h"
 #include "fa_fwd_bf16_pipe.h"
 #include "fa_fwd_f32.h"
+#include "fa_bwd_bf16.h"
 
 namespace {
 
@@ -141,9 +142,114 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     return FA_OK;
 }
 
+using BwdKernel = void (*)(fa::BwdArgs);
+
+template <int D>
+void pick_bwd(int mask_kind, BwdKernel& dkdv, BwdKernel& dq) {
+    switch (mask_kind) {
+        case 0: dkdv = fa::fa_bwd_dkdv_kernel<D, false, false>; dq = fa::fa_bwd_dq_kernel<D, false, false>; break;
+        case 1: dkdv = fa::fa_bwd_dkdv_kernel<D, true, false>; dq = fa::fa_bwd_dq_kernel<D, true, false>; break;
+        case 2: dkdv = fa::fa_bwd_dkdv_kernel<D, false, true>; dq = fa::fa_bwd_dq_kernel<D, false, true>; break;
+        default: dkdv = fa::fa_bwd_dkdv_kernel<D, true, true>; dq = fa::fa_bwd_dq_kernel<D, true, true>; break;
+    }
+}
+
+bool launched_ok() {
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) {
+        g_last_hip_error = static_cast<int>(err);
+        return false;
+    }
+    return true;
+}
+
+int bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+               float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
+               int mask_kind, const int32_t* seqlens, int in_dtype, int grad_dtype, void* stream) {
+    // ---- validation (host only, before any HIP call) ----
+    if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
+    if (mask_kind < 0 || mask_kind > (FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (grad_dtype != FA_DTYPE_F32 && grad_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (d <= 0) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (in_dtype != FA_DTYPE_BF16 || grad_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || N == 0) return FA_OK;
+    if (!q || !k || !v || !o || !lse || !dout || !delta || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+    if ((mask_kind & FA_MASK_KEY_PADDING) && !seqlens) return FA_ERR_INVALID_ARG;
+    const void* t16[] = {q, k, v, o, dout, dq, dk, dv};
+    for (const void* p : t16)
+        if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+    if (!aligned(lse, 4) || !aligned(delta, 4)) return FA_ERR_INVALID_ARG;
+    if ((mask_kind & FA_MASK_KEY_PADDING) && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
+    // sizes: element offsets are 64-bit in the kernels; workgroup counts must fit in 32 bits
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    const int64_t n_blk = (static_cast<int64_t>(N) + 127) / 128;
+    if (bh * n_blk > 0x7fffffff || bh * N / 8 + 1 > 0x7fffffff) return FA_ERR_INVALID_ARG;
+    // outputs (the gradients and the workspace) must not overlap each other or any input
+    const size_t in_b = static_cast<size_t>(bh) * N * d * 2, g_b = static_cast<size_t>(bh) * N * d * 4;
+    const size_t row_b = static_cast<size_t>(bh) * N * 4;
+    const void* outs[] = {dq, dk, dv, delta};
+    const size_t out_sz[] = {g_b, g_b, g_b, row_b};
+    const void* ins[] = {q, k, v, o, dout, lse};
+    const size_t in_sz[] = {in_b, in_b, in_b, in_b, in_b, row_b};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_INVALID_ARG;
+    }
+
+    fa::BwdArgs args;
+    args.q = q;
+    args.k = k;
+    args.v = v;
+    args.o = o;
+    args.dout = dout;
+    args.lse = lse;
+    args.delta = delta;
+    args.dq = static_cast<float*>(dq);
+    args.dk = static_cast<float*>(dk);
+    args.dv = static_cast<float*>(dv);
+    args.seqlens = (mask_kind & FA_MASK_KEY_PADDING) ? seqlens : nullptr;
+    args.B = B;
+    args.H = H;
+    args.N = N;
+    args.scale = scale;
+    args.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+
+    BwdKernel dkdv, dqk;
+    void (*delta_k)(fa::BwdArgs);
+    if (d == 64) {
+        pick_bwd<64>(mask_kind, dkdv, dqk);
+        delta_k = fa::fa_bwd_delta_kernel<64>;
+    } else {
+        pick_bwd<128>(mask_kind, dkdv, dqk);
+        delta_k = fa::fa_bwd_delta_kernel<128>;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t rows_per_blk = 256 / (d / 8);
+    hipLaunchKernelGGL(delta_k, dim3(static_cast<unsigned>((bh * N + rows_per_blk - 1) / rows_per_blk)),
+                       dim3(kThreads), 0, st, args);
+    if (!launched_ok()) return FA_ERR_HIP;
+    hipLaunchKernelGGL(dkdv, dim3(static_cast<unsigned>(bh * n_blk)), dim3(kThreads), 0, st, args);
+    if (!launched_ok()) return FA_ERR_HIP;
+    hipLaunchKernelGGL(dqk, dim3(static_cast<unsigned>(bh * n_blk)), dim3(kThreads), 0, st, args);
+    if (!launched_ok()) return FA_ERR_HIP;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int mask_kind,
+           const int32_t* seqlens, int in_dtype, int grad_dtype, void* stream) {
+    return bwd_launch(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask_kind, seqlens, in_dtype,
+                      grad_dtype, stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype, int out_dtype,

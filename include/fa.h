@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 10000 /* major*10000 + minor*100 + patch */
+#define FA_VERSION 10100 /* major*10000 + minor*100 + patch */
 
 typedef enum {
     FA_OK = 0,
@@ -91,6 +91,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
                    int in_dtype, int out_dtype, void* stream, int variant);
+
+/*
+ * fa_bwd -- gradients of the forward pass with respect to Q, K and V.
+ *
+ * With P the attention probabilities of the forward pass (masked keys have P = 0) and dO the
+ * gradient arriving at O:
+ *     dV = P^T dO,   dP = dO V^T,   D_i = dO_i . O_i,   dS = P * (dP - D),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q.
+ * Only O receives a gradient; the LSE output is not differentiated.  P is recomputed tile by
+ * tile from Q, K and the LSE saved by fa_fwd instead of being stored ("FlashAttention Interview
+ * Questions: IO Complexity, Tiling, and Numerical Stability" (cswork.org), section "Why can
+ * recomputation help training?"), so no N x N buffer exists.
+ *
+ *   q, k, v, o, dout  [B, H, N, d] device tensors of `in_dtype`, 16-byte aligned: the forward
+ *             inputs, its output O and the upstream gradient dO.
+ *   lse       [B, H, N] float32, 4-byte aligned: the natural-log LSE fa_fwd wrote for these
+ *             inputs (rows with no visible key hold -inf and receive no gradient).
+ *   delta     [B, H, N] float32 workspace owned by the caller, 4-byte aligned; receives
+ *             D_i = dO_i . O_i.
+ *   dq, dk, dv  [B, H, N, d] device tensors of `grad_dtype`, 16-byte aligned; written.  Keys no
+ *             row may see (masked, or past seqlens[b]) get zero gradient.
+ *   B, H, N, d, scale, mask_kind, seqlens, stream   as for fa_fwd.
+ *   in_dtype, grad_dtype   supported: (BF16, F32) with d in {64, 128}.  P and dS enter the
+ *             value and key products as bf16 values with float32 accumulation.
+ * dq, dk, dv and delta must not overlap each other or any input.  Three kernels are enqueued on
+ * `stream`; there are no atomics, so results are identical from run to run.
+ * Returns an fa_status (validation as for fa_fwd, before any HIP call).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, float* delta, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
+           int in_dtype, int grad_dtype, void* stream);
 
 /* Number of kernel variants fa_fwd_variant accepts (variants are 0 .. count-1). */
 int fa_variant_count(void);

@@ -126,6 +126,37 @@ def test_empty_problem_is_a_noop(dims):
     assert fa.fa_fwd(None, None, None, None, None, B, H, N, 128, 0.125, 3, None, BF16, F32, None) == fa.FA_OK
 
 
+def bwd_call(q=P, k=P2, v=P3, o=P4, lse=P4 + (1 << 26), dout=P + (1 << 26), delta=P2 + (1 << 26),
+             dq=P3 + (1 << 26), dk=P + (1 << 27), dv=P2 + (1 << 27), B=1, H=1, N=16, d=64, scale=0.125, mask=0,
+             seqlens=None, ind=BF16, gd=F32):
+    return fa.fa_bwd(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask, seqlens, ind, gd, None)
+
+
+BWD_INVALID = {
+    "null q": dict(q=None), "null lse": dict(lse=None), "null dout": dict(dout=None),
+    "null delta": dict(delta=None), "null dq": dict(dq=None), "null dv": dict(dv=None),
+    "negative N": dict(N=-1), "mask bit 4": dict(mask=4), "padding without seqlens": dict(mask=2),
+    "nan scale": dict(scale=float("nan")), "misaligned o": dict(o=P4 + 2), "misaligned dk": dict(dk=P + (1 << 27) + 8),
+    "misaligned delta": dict(delta=P2 + (1 << 26) + 2), "dq aliases q": dict(dq=P), "dk overlaps dv": dict(dk=P2 + (1 << 27) + 64),
+    "delta inside dq": dict(delta=P3 + (1 << 26) + 64), "bad grad dtype": dict(gd=5), "d zero": dict(d=0),
+}
+BWD_UNSUPPORTED = {"d 96": dict(d=96), "f32 inputs": dict(ind=F32), "bf16 gradients": dict(gd=BF16)}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_INVALID))
+def test_bwd_invalid_argument_rejected_on_host(name):
+    assert bwd_call(**BWD_INVALID[name]) == fa.FA_ERR_INVALID_ARG, name
+
+
+@pytest.mark.parametrize("name", sorted(BWD_UNSUPPORTED))
+def test_bwd_unsupported_rejected_on_host(name):
+    assert bwd_call(**BWD_UNSUPPORTED[name]) == fa.FA_ERR_UNSUPPORTED, name
+
+
+def test_bwd_empty_problem_is_a_noop():
+    assert fa.fa_bwd(*([None] * 10), 0, 4, 16, 64, 0.125, 1, None, BF16, F32, None) == fa.FA_OK
+
+
 def test_python_forward_rejects_host_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
