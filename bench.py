@@ -143,6 +143,8 @@ def main() -> int:
                     help="override the workload's Q/K gain (c3 uses 3: logit std ~ 9; 1 gives flat rows)")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (fa_bwd: dQ, dK, dV) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only the known-size copy used to calibrate the byte counters")
     args = ap.parse_args()
@@ -186,6 +188,23 @@ def main() -> int:
         fa.forward(q, k, v, scale=x.scale, causal=causal, seqlens=seq, out_dtype=out_dtype,
                    out=o, lse_out=lse, variant=args.variant)
 
+    if args.bwd:
+        # the forward's bf16 output and LSE, and a seeded upstream gradient of the same shape
+        if q.dtype != torch.bfloat16:
+            print("bench.py: the backward pass takes bf16 inputs", file=sys.stderr)
+            return 1
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        out_dtype = torch.bfloat16
+        step()
+        g = torch.Generator("cpu").manual_seed(w.seed + 1000)
+        dout = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(dev)
+        grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+        def step():
+            fa.backward(q, k, v, o, lse, dout, scale=x.scale, causal=causal, seqlens=seq, out=grads,
+                        delta=delta)
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -208,6 +227,8 @@ def main() -> int:
     ms_per_step = wall / args.steps * 1e3
 
     flops = counted_flops(w.B, w.H, w.N, w.d, causal)
+    if args.bwd:   # five products of the forward's size (S, dP, dV, dK, dQ): 2.5x the forward
+        flops *= 2.5
     value = flops / (wall / args.steps) / 1e12
     fp32 = w.in_dtype == torch.float32
     nbytes = compulsory_bytes(w.B, w.H, w.N, w.d, 4 if fp32 else 2, 4 if out_dtype == torch.float32 else 2)
@@ -222,7 +243,7 @@ def main() -> int:
     traffic = recorded_traffic(workload_id)
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if not args.bwd else "attention bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's FLOP), 1 GPU",
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -241,6 +262,7 @@ def main() -> int:
                          + f"{'fp32' if out_dtype == torch.float32 else 'bf16'} out, fp32 LSE"),
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name,
             "flop_per_step": flops, "compulsory_bytes_per_step": nbytes, "variant": args.variant,
+            "pass": "backward" if args.bwd else "forward",
         },
         "roofline": {
             "bound": bound,
@@ -252,7 +274,11 @@ def main() -> int:
             "kernel_avg_ms": round(avg_launch_s * 1e3, 5),
         },
     }
-    if not args.no_cpu_baseline:
+    if args.bwd:
+        res["roofline"]["note"] = ("three kernels per step (row term, dK/dV, dQ); achieved counts the pass's "
+                                   "2.5x-forward FLOP over their combined time, which executes 3.5x")
+        res["roofline"]["traffic"] = None
+    if not args.no_cpu_baseline and not args.bwd:
         print(f"[bench] timing the fp64 oracle on {args.cpu_rows} rows per head", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_rows, w.N))
     print(json.dumps(res), flush=True)

@@ -146,9 +146,11 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdArgs a) {
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = a.N;
-    const int nkb = (N + BK - 1) / BK;
-    const int bh = blockIdx.x / nkb;
-    const int k0 = (blockIdx.x % nkb) * BK;
+    // Work items in decreasing work order across all heads: under the causal mask key block kb
+    // meets N/32 - 4kb query tiles, so every head's block 0 runs first, then every block 1 ...
+    const int BH = a.B * a.H;
+    const int bh = blockIdx.x % BH;
+    const int k0 = (blockIdx.x / BH) * BK;
     const int b = bh / a.H;
     const int64_t base = (int64_t)bh * N * D;
     int Lk = N;
@@ -273,9 +275,12 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
     const int l32 = lane & 31;
     const int hh = lane >> 5;
     const int N = a.N;
+    // Work items in decreasing work order across all heads: under the causal mask query block
+    // qb meets qb + 1 key blocks, so every head's last block runs first
     const int nqb = (N + BM - 1) / BM;
-    const int bh = blockIdx.x / nqb;
-    const int q0 = (blockIdx.x % nqb) * BM;
+    const int BH = a.B * a.H;
+    const int bh = blockIdx.x % BH;
+    const int q0 = (CAUSAL ? nqb - 1 - blockIdx.x / BH : blockIdx.x / BH) * BM;
     const int b = bh / a.H;
     const int64_t base = (int64_t)bh * N * D;
     int Lk = N;
