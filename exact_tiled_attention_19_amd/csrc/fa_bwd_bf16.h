@@ -12,13 +12,14 @@
 // Three kernels, all on one stream, none with atomics (the result is run-to-run identical):
 //   fa_bwd_delta_kernel  D_i = dO_i . O_i for every row, into the caller's float32 workspace.
 //   fa_bwd_dkdv_kernel   one workgroup per (batch, head, 128 keys), 32 keys per wave; the
-//                        wave's K^T and V^T stay in VGPRs while 32-row tiles of Q and dO stream
-//                        through LDS.  Per tile: S = Q K^T and dP = dO V^T (MFMA, A from LDS,
+//                        wave's K^T and V^T stay in VGPRs while 64-row tiles of Q and dO stream
+//                        through double-buffered LDS (one barrier per tile).  Per tile: S = Q K^T and dP = dO V^T (MFMA, A from LDS,
 //                        B from VGPRs); P and dS elementwise; dV^T += dO^T P and
 //                        dK^T += Q^T dS (MFMA, A read from LDS with the transpose read, B
 //                        straight from the S/dP accumulator registers).
 //   fa_bwd_dq_kernel     one workgroup per (batch, head, 128 query rows), 32 rows per wave;
-//                        Q^T and dO^T in VGPRs while 64-key tiles of K and V stream through LDS.
+//                        Q^T and dO^T in VGPRs while 64-key tiles of K and V stream through
+//                        double-buffered LDS.
 //                        Per tile: S^T = K Q^T and dP^T = V dO^T; P^T and dS^T elementwise;
 //                        dQ^T += K^T dS^T.
 // In every 32x32 accumulator a lane owns one column (a key in dkdv, a query row in dq) and 16
@@ -128,17 +129,26 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
     if (row < rows && part == 0) a.delta[row] = s;
 }
 
+// Query rows per dK/dV tile.  d = 64: 32-row tiles keep two workgroups per CU.  d = 128 runs
+// one workgroup per CU; under the causal mask it takes 64-row tiles (two 32-row halves, so one
+// half's vector work can overlap the other's MFMAs), which in the unmasked variant would not
+// fit the register file.
+template <int D, bool CAUSAL>
+constexpr int bwd_bq() { return D == 128 && CAUSAL ? 64 : 32; }
+
 template <int D, bool CAUSAL, bool PAD>
-__global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int BK = 128;        // keys per workgroup (32 per wave)
-    constexpr int BQ = 32;         // query rows per tile
+    constexpr int BQ = bwd_bq<D, CAUSAL>();  // query rows per tile, handled as 32-row halves
+    constexpr int NH = BQ / 32;
     constexpr int KC = D / 16;     // k-steps over d
     constexpr int NDB = D / 32;    // 32-wide blocks of d
     constexpr int TILEB = BQ * D * 2;
-    __shared__ __attribute__((aligned(1024))) unsigned char qs[TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char dos[TILEB];
-    __shared__ float lse2s[BQ];
-    __shared__ float dls[BQ];
+    // double-buffered Q and dO tiles: tile t+1 is stored while tile t is read, one barrier a tile
+    __shared__ __attribute__((aligned(1024))) unsigned char qs[2][TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char dos[2][TILEB];
+    __shared__ __attribute__((aligned(16))) float lse2s[2][BQ];
+    __shared__ __attribute__((aligned(16))) float dls[2][BQ];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -147,7 +157,7 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdArgs a) {
     const int hh = lane >> 5;
     const int N = a.N;
     // Work items in decreasing work order across all heads: under the causal mask key block kb
-    // meets N/32 - 4kb query tiles, so every head's block 0 runs first, then every block 1 ...
+    // meets (N - 128 kb) / BQ query tiles, so every head's block 0 runs first, then every block 1
     const int BH = a.B * a.H;
     const int bh = blockIdx.x % BH;
     const int k0 = (blockIdx.x / BH) * BK;
@@ -158,7 +168,8 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdArgs a) {
         const int s = a.seqlens[b];
         Lk = s < 0 ? 0 : (s > N ? N : s);
     }
-    const int key = k0 + wave * 32 + l32;    // this lane's key (column of every accumulator)
+    const int kw0 = k0 + wave * 32;          // first key of this wave
+    const int key = kw0 + l32;               // this lane's key (column of every accumulator)
 
     // K^T and V^T as B operands ([k = d][n = key]): lane (key, hh) holds X[key][16c + 8hh ..]
     bf16x8 kt[KC], vt[KC];
@@ -178,7 +189,7 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdArgs a) {
 
     const int nt = (N + BQ - 1) / BQ;
     const int t0 = CAUSAL ? k0 / BQ : 0;        // earlier rows see none of these keys
-    const bool live = k0 < Lk;                    // some key of this block is visible at all
+    const int t_begin = k0 < Lk ? t0 : nt;       // no visible key at all: nothing to accumulate
     const uint16_t* qg = (const uint16_t*)a.q + base;
     const uint16_t* dog = (const uint16_t*)a.dout + base;
     const float* lse_g = a.lse + (int64_t)bh * N;
@@ -194,52 +205,94 @@ __global__ void __launch_bounds__(256, 1) fa_bwd_dkdv_kernel(BwdArgs a) {
             pdl = g < N ? dl_g[g] : 0.f;
         }
     };
-    if (live && t0 < nt) fetch(t0);
-    for (int t = live ? t0 : nt; t < nt; ++t) {
-        __syncthreads();                 // the previous tile is no longer read
-        sq.stash(qs, tid);
-        sdo.stash(dos, tid);
+    auto stash = [&](int buf) __attribute__((always_inline)) {
+        sq.stash(qs[buf], tid);
+        sdo.stash(dos[buf], tid);
         if (tid < BQ) {
-            lse2s[tid] = plse;
-            dls[tid] = pdl;
+            lse2s[buf][tid] = plse;
+            dls[buf][tid] = pdl;
         }
-        __syncthreads();
-        if (t + 1 < nt) fetch(t + 1);    // next tile's global loads overlap this tile's work
+    };
+    if (t_begin < nt) {
+        fetch(t_begin);
+        stash(t_begin & 1);
+    }
+    __syncthreads();
+    for (int t = t_begin; t < nt; ++t) {
+        const int cur = t & 1;
+        if (t + 1 < nt) fetch(t + 1);            // global loads overlap this tile's work
+        const unsigned char* qt_ = qs[cur];
+        const unsigned char* dt_ = dos[cur];
+        const float* ls = lse2s[cur];
+        const float* dd = dls[cur];
+        const int r0 = t * BQ;
+        // the mask matters only where some row may not see some key of this wave (causal
+        // diagonal, keys past the valid length or past N, rows past N)
+        const bool masked = (CAUSAL && r0 < kw0 + 31) || kw0 + 32 > Lk || r0 + BQ > N;
 
-        // S = Q K^T and dP = dO V^T: lane (key, hh) holds rows 8(r/4) + 4hh + r%4 of the tile
-        f32x16 s = {}, dp = {};
+        // S = Q K^T and dP = dO V^T per 32-row half: lane (key, hh) holds half rows
+        // 8(r/4) + 4hh + r%4.  Computed inside each arm of the mask branch below, so that one
+        // basic block holds the whole tile and half 0's vector work can overlap half 1's MFMAs.
+        f32x16 s[NH], dp[NH];
+        auto sdp = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(qs, 0, l32, hh, c), kt[c], s, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(dos, 0, l32, hh, c), vt[c], dp, 0, 0, 0);
-        }
-        // P = exp(scale s - LSE) on visible (row, key) pairs, dS = P (dP - D)
-        u32x4 ph[2], dsh[2];
+            for (int h = 0; h < NH; ++h) {
+                s[h] = dp[h] = f32x16{};
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-            float p[2], ds[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int rr = 8 * ((r + u) >> 2) + 4 * hh + ((r + u) & 3);
-                const int g = t * BQ + rr;
-                const bool ok = g < N && key < Lk && (!CAUSAL || key <= g);
-                const float e = fast_exp2(fmaf(s[r + u], a.scale_log2, -lse2s[rr]));
-                p[u] = ok ? e : 0.f;
-                ds[u] = p[u] * (dp[r + u] - dls[rr]);
+                for (int c = 0; c < KC; ++c) {
+                    s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c), kt[c], s[h], 0, 0, 0);
+                    dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c), vt[c], dp[h], 0, 0, 0);
+                }
             }
-            ph[r / 8][(r % 8) / 2] = pack_bf16x2(p[0], p[1]);
-            dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS (k runs over the tile's rows)
+        };
+        // P = exp(scale s - LSE) on visible pairs, dS = P (dP - D); then dV^T += dO^T P and
+        // dK^T += Q^T dS over the half's rows.  Half 1's products overlap half 0's vector work.
+        auto half = [&](int h, auto masked_c) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            u32x4 ph[2], dsh[2];
 #pragma unroll
-        for (int pc = 0; pc < 2; ++pc)
+            for (int r = 0; r < 16; r += 4) {
+                const int rr = 32 * h + 8 * (r >> 2) + 4 * hh;       // rows rr .. rr+3
+                const f32x4 l4 = *(const f32x4*)(ls + rr);
+                const f32x4 d4 = *(const f32x4*)(dd + rr);
+                float p[4], ds[4];
 #pragma unroll
-            for (int db = 0; db < NDB; ++db) {
-                dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(dos, l32, hh, pc, db),
-                                                                 __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
-                dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(qs, l32, hh, pc, db),
-                                                                 __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                for (int u = 0; u < 4; ++u) {
+                    float e = fast_exp2(fmaf(s[h][r + u], a.scale_log2, -l4[u]));
+                    if constexpr (MASKED) {
+                        const int g = r0 + rr + u;
+                        const bool ok = g < N && key < Lk && (!CAUSAL || key <= g);
+                        e = ok ? e : 0.f;
+                    }
+                    p[u] = e;
+                    ds[u] = e * (dp[h][r + u] - d4[u]);
+                }
+                ph[r / 8][(r % 8) / 2] = pack_bf16x2(p[0], p[1]);
+                ph[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(p[2], p[3]);
+                dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
+                dsh[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(ds[2], ds[3]);
             }
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(dt_, l32, hh, 2 * h + pc, db),
+                                                                     __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
+                    dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(qt_, l32, hh, 2 * h + pc, db),
+                                                                     __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                }
+        };
+        if (masked) {
+            sdp();
+#pragma unroll
+            for (int h = 0; h < NH; ++h) half(h, std::true_type{});
+        } else {
+            sdp();
+#pragma unroll
+            for (int h = 0; h < NH; ++h) half(h, std::false_type{});
+        }
+        if (t + 1 < nt) stash((t + 1) & 1);
+        __syncthreads();
     }
     // register r of block db is X^T[32db + 8(r/4) + 4hh + r%4][key]
     if (key < N) {
@@ -264,10 +317,9 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
     constexpr int KC = D / 16;
     constexpr int NKB = BN / 32;
     constexpr int NDB = D / 32;
-    constexpr int PC = BN / 16;
     constexpr int TILEB = BN * D * 2;
-    __shared__ __attribute__((aligned(1024))) unsigned char ks[TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vs[TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char ks[2][TILEB];
+    __shared__ __attribute__((aligned(1024))) unsigned char vs[2][TILEB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -288,7 +340,8 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
         const int s = a.seqlens[b];
         Lk = s < 0 ? 0 : (s > N ? N : s);
     }
-    const int row = q0 + wave * 32 + l32;    // this lane's query row (column of every accumulator)
+    const int qw0 = q0 + wave * 32;          // first query row of this wave
+    const int row = qw0 + l32;               // this lane's query row (column of every accumulator)
     const bool row_ok = row < N;
 
     // Q^T and dO^T as B operands ([k = d][n = row])
@@ -318,49 +371,77 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
     if (nj > 0) {
         sk.fetch(kg, 0, N, tid);
         sv.fetch(vg, 0, N, tid);
+        sk.stash(ks[0], tid);
+        sv.stash(vs[0], tid);
     }
+    __syncthreads();
     for (int j = 0; j < nj; ++j) {
-        __syncthreads();
-        sk.stash(ks, tid);
-        sv.stash(vs, tid);
-        __syncthreads();
+        const int cur = j & 1;
         if (j + 1 < nj) {
             sk.fetch(kg, (j + 1) * BN, N, tid);
             sv.fetch(vg, (j + 1) * BN, N, tid);
         }
-        // S^T = K Q^T, dP^T = V dO^T: lane (row, hh) holds keys 32kb + 8(r/4) + 4hh + r%4
+        const unsigned char* kt_ = ks[cur];
+        const unsigned char* vt_ = vs[cur];
+        const int j0 = j * BN;
+        // the mask matters only where some key of the tile lies past a row of this wave (causal
+        // diagonal) or past the valid length (and past N)
+        const bool masked = (CAUSAL && j0 + BN - 1 > qw0) || j0 + BN > Lk;
+        // S^T = K Q^T, dP^T = V dO^T per 32-key block: lane (row, hh) holds keys
+        // 32kb + 8(r/4) + 4hh + r%4 (inside each arm of the mask branch, as in the dK/dV kernel)
         f32x16 s[NKB], dp[NKB];
+        auto sdp = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            s[kb] = dp[kb] = f32x16{};
+            for (int kb = 0; kb < NKB; ++kb) {
+                s[kb] = dp[kb] = f32x16{};
 #pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(ks, 32 * kb, l32, hh, c), qt[c], s[kb], 0, 0, 0);
-                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(vs, 32 * kb, l32, hh, c), dot[c], dp[kb], 0, 0, 0);
+                for (int c = 0; c < KC; ++c) {
+                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(kt_, 32 * kb, l32, hh, c), qt[c], s[kb], 0, 0, 0);
+                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(vt_, 32 * kb, l32, hh, c), dot[c], dp[kb], 0, 0, 0);
+                }
             }
-        }
-        // dS^T = P^T (dP^T - D) on visible pairs, packed as the B operand of dQ^T += K^T dS^T
-        u32x4 dsh[PC];
+        };
+        // dS^T = P^T (dP^T - D) on visible pairs, packed as the B operand of dQ^T += K^T dS^T;
+        // block 1's products overlap block 0's vector work
+        auto block = [&](int kb, auto masked_c) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            u32x4 dsh[2];
 #pragma unroll
-        for (int f = 0; f < 16 * NKB; f += 2) {
-            float ds[2];
+            for (int r = 0; r < 16; r += 2) {
+                float ds[2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int kb = (f + u) / 16, r = (f + u) % 16;
-                const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool ok = key < Lk && (!CAUSAL || key <= row);
-                const float e = fast_exp2(fmaf(s[kb][r], a.scale_log2, -lse2));
-                const float p = ok ? e : 0.f;
-                ds[u] = p * (dp[kb][r] - dl);
+                for (int u = 0; u < 2; ++u) {
+                    float e = fast_exp2(fmaf(s[kb][r + u], a.scale_log2, -lse2));
+                    if constexpr (MASKED) {
+                        const int key = j0 + 32 * kb + 8 * ((r + u) >> 2) + 4 * hh + ((r + u) & 3);
+                        const bool ok = key < Lk && (!CAUSAL || key <= row);
+                        e = ok ? e : 0.f;
+                    }
+                    ds[u] = e * (dp[kb][r + u] - dl);
+                }
+                dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
             }
-            dsh[f / 8][(f % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc)
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+                    dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(kt_, l32, hh, 2 * kb + pc, db),
+                                                                     __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
+        };
+        if (masked) {
+            sdp();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) block(kb, std::true_type{});
+        } else {
+            sdp();
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) block(kb, std::false_type{});
         }
-#pragma unroll
-        for (int pc = 0; pc < PC; ++pc)
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(ks, l32, hh, pc, db),
-                                                                 __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
+        if (j + 1 < nj) {
+            sk.stash(ks[cur ^ 1], tid);
+            sv.stash(vs[cur ^ 1], tid);
+        }
+        __syncthreads();
     }
     if (row_ok) {
 #pragma unroll
