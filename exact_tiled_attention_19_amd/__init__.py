@@ -1,10 +1,13 @@
 """Fused exact-attention forward for AMD Instinct MI355X (gfx950).
 
-``forward(q, k, v, ...)`` and ``backward(q, k, v, o, lse, dout, ...)`` run the HIP kernels of ``libfa.so`` through its C ABI
+``forward(q, k, v, ...)``, ``forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, ...)`` and
+``backward(q, k, v, o, lse, dout, ...)`` run the HIP kernels of ``libfa.so`` through its C ABI
 (include/fa.h); PyTorch only supplies device memory and the stream.
 """
 
 from .binding import (  # noqa: F401
+    FA_ALIGN_BOTTOM_RIGHT,
+    FA_ALIGN_TOP_LEFT,
     FA_DTYPE_BF16,
     FA_DTYPE_F32,
     FA_ERR_HIP,
@@ -21,9 +24,12 @@ from .binding import (  # noqa: F401
     backward,
     fa_bwd,
     fa_fwd,
+    fa_fwd_varlen,
     forward,
+    forward_varlen,
     load_library,
     status_str,
     variant_count,
+    varlen_workspace_size,
     version,
 )

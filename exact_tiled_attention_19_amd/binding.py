@@ -29,6 +29,10 @@ FA_MASK_KEY_PADDING = 2
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
 
+FA_ALIGN_BOTTOM_RIGHT = 0
+FA_ALIGN_TOP_LEFT = 1
+_ALIGN_CODE = {"bottom_right": FA_ALIGN_BOTTOM_RIGHT, "top_left": FA_ALIGN_TOP_LEFT}
+
 _DTYPE_CODE = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16}
 
 # Every symbol include/fa.h declares, with its ctypes signature.
@@ -39,6 +43,9 @@ SIGNATURES = {
     "fa_fwd_variant": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP, _I]),
     "fa_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I,
                     _VP]),
+    "fa_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I,
+                           _VP, ctypes.c_size_t, _I, _I, _VP]),
+    "fa_fwd_varlen_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_variant_count": (_I, []),
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
@@ -215,6 +222,86 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
                 _ptr(out[2]), B, H, N, d, float(scale), mask, _ptr(seqlens), FA_DTYPE_BF16, FA_DTYPE_F32, stream)
     _check(st)
     return out
+
+
+def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, max_k, d, scale, mask_kind,
+                  causal_align, workspace, workspace_bytes, in_dtype, out_dtype, stream) -> int:
+    """Raw call of the packed variable-length forward through the C ABI (pointers as ints or None)."""
+    return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, max_k, d,
+                                        ctypes.c_float(scale), mask_kind, causal_align, workspace, workspace_bytes,
+                                        in_dtype, out_dtype, stream)
+
+
+def varlen_workspace_size(B: int, H: int, max_seqlen_q: int, max_seqlen_k: int, d: int) -> int:
+    return int(load_library().fa_fwd_varlen_workspace_size(B, H, max_seqlen_q, max_seqlen_k, d))
+
+
+def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                   cu_seqlens_k: torch.Tensor, max_seqlen_q: Optional[int] = None,
+                   max_seqlen_k: Optional[int] = None, *, scale: Optional[float] = None, causal: bool = False,
+                   align: str = "bottom_right", out_dtype: Optional[torch.dtype] = None, return_lse: bool = True,
+                   out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Exact attention over a packed batch of sequences on the GPU: returns (O, LSE).
+
+    q: [Tq, H, d], k, v: [Tk, H, d] contiguous bfloat16 device tensors (token-major).
+    cu_seqlens_q, cu_seqlens_k: contiguous int32 device tensors [B + 1], prefix sums of the
+    per-sequence query and key lengths.  max_seqlen_q / max_seqlen_k: the longest lengths (read
+    from the prefix sums, with a device synchronisation, when omitted).
+    causal: key j visible to query row i iff j <= i + delta, delta = Lk - Lq for
+    align="bottom_right" and 0 for align="top_left".
+    Returns O [Tq, H, d] (out_dtype, default bfloat16) and LSE [H, Tq] float32.
+    workspace: optional uint8 device tensor of at least ``varlen_workspace_size(...)`` bytes.
+    """
+    ts = (q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if not all(t.is_cuda for t in ts):
+        raise ValueError("all tensors must be device tensors")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape or q.shape[1:] != k.shape[1:]:
+        raise ValueError("q must be [Tq, H, d] and k, v [Tk, H, d]")
+    if not all(t.is_contiguous() for t in ts):
+        raise ValueError("all tensors must be contiguous")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32 or cu_seqlens_q.dim() != 1 \
+            or cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be int32 [B + 1] tensors")
+    if align not in _ALIGN_CODE:
+        raise ValueError(f"align must be one of {sorted(_ALIGN_CODE)}")
+    Tq, H, d = q.shape
+    Tk = k.shape[0]
+    B = cu_seqlens_q.numel() - 1
+    if max_seqlen_q is None:
+        max_seqlen_q = int((cu_seqlens_q[1:] - cu_seqlens_q[:-1]).max().item()) if B > 0 else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int((cu_seqlens_k[1:] - cu_seqlens_k[:-1]).max().item()) if B > 0 else 0
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty((Tq, H, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous() or out.device != q.device:
+        raise ValueError("out has the wrong shape, dtype, layout or device")
+    lse = None
+    if return_lse:
+        if lse_out is None:
+            lse = torch.empty((H, Tq), dtype=torch.float32, device=q.device)
+        else:
+            if lse_out.shape != (H, Tq) or lse_out.dtype != torch.float32 or not lse_out.is_contiguous():
+                raise ValueError("lse_out must be a contiguous float32 [H, Tq] tensor")
+            lse = lse_out
+    ws_bytes = varlen_workspace_size(B, H, max_seqlen_q, max_seqlen_k, d)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_given = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H,
+                       Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
+                       FA_MASK_CAUSAL if causal else FA_MASK_NONE, _ALIGN_CODE[align], _ptr(workspace), ws_given,
+                       FA_DTYPE_BF16, _DTYPE_CODE[out_dtype], stream)
+    _check(st)
+    return out, lse
 
 
 def variant_count() -> int:

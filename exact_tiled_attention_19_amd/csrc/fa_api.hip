@@ -11,6 +11,7 @@
 #include "fa_fwd_bf16_pipe.h"
 #include "fa_fwd_f32.h"
 #include "fa_bwd_bf16.h"
+#include "fa_decode_bf16.h"
 
 namespace {
 
@@ -240,9 +241,197 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     return FA_OK;
 }
 
+// ---- packed variable-length sequences ------------------------------------------------------
+
+// Query sequences of at most this many rows take the split-key decoding kernel; longer ones the
+// pipelined tile kernel.
+constexpr int kDecodeMaxRows = 4;
+// Workgroups the decoding kernel aims for (8 per CU), and the fewest keys per range.
+constexpr int64_t kDecodeTargetWgs = 2048;
+constexpr int64_t kDecodeMinKeys = 256;
+
+struct DecodePlan {
+    int g;            // query rows per sequence the kernel handles (0: not a decoding shape)
+    int n_splits;     // key ranges per (sequence, head)
+    int chunk;        // keys per range
+    size_t ws_bytes;  // workspace for the partial states (0 with one range)
+};
+
+// A pure function of the sizes, so the caller can size the workspace before the call.
+DecodePlan decode_plan(int B, int H, int max_q, int max_k, int d) {
+    DecodePlan p{0, 1, 0, 0};
+    if (max_q <= 0 || max_q > kDecodeMaxRows || B <= 0 || H <= 0 || max_k < 0 || (d != 64 && d != 128)) return p;
+    p.g = max_q == 1 ? 1 : kDecodeMaxRows;
+    const int64_t step = d == 128 ? fa::dec_keys_per_step<128>() : fa::dec_keys_per_step<64>();
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    int64_t S = (kDecodeTargetWgs + bh - 1) / bh;
+    const int64_t smax = (max_k + kDecodeMinKeys - 1) / kDecodeMinKeys;
+    S = S < smax ? S : smax;
+    S = S < 1 ? 1 : S;
+    int64_t chunk = (max_k + S - 1) / S;
+    chunk = (chunk + step - 1) / step * step;
+    if (chunk < step) chunk = step;
+    S = (max_k + chunk - 1) / chunk;
+    if (S < 1) S = 1;
+    p.n_splits = static_cast<int>(S);
+    p.chunk = static_cast<int>(chunk);
+    p.ws_bytes = S > 1 ? static_cast<size_t>(bh) * S * p.g * (d + 2) * sizeof(float) : 0;
+    return p;
+}
+
+template <int D, bool OUTF32>
+Kernel pick_varlen(bool causal) {
+    return causal ? fa::fa_fwd_bf16_varlen_kernel<D, 64, 1, true, OUTF32> : fa::fa_fwd_bf16_varlen_kernel<D, 64, 1, false, OUTF32>;
+}
+
+using DecKernel = void (*)(fa::DecArgs);
+
+template <int D, bool OUTF32>
+void pick_decode(int g, bool causal, DecKernel& main, DecKernel& merge) {
+    if (g == 1) {
+        main = causal ? fa::fa_decode_kernel<D, 1, true, OUTF32> : fa::fa_decode_kernel<D, 1, false, OUTF32>;
+        merge = fa::fa_decode_merge_kernel<D, 1, OUTF32>;
+    } else {
+        main = causal ? fa::fa_decode_kernel<D, kDecodeMaxRows, true, OUTF32>
+                      : fa::fa_decode_kernel<D, kDecodeMaxRows, false, OUTF32>;
+        merge = fa::fa_decode_merge_kernel<D, kDecodeMaxRows, OUTF32>;
+    }
+}
+
+int varlen_launch(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
+                  const int32_t* cu_k, int B, int H, int total_q, int total_k, int max_q, int max_k, int d,
+                  float scale, int mask_kind, int causal_align, void* workspace, size_t workspace_bytes,
+                  int in_dtype, int out_dtype, void* stream) {
+    // ---- validation (host only, before any HIP call) ----
+    if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return FA_ERR_INVALID_ARG;
+    if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;
+    if (causal_align != FA_ALIGN_BOTTOM_RIGHT && causal_align != FA_ALIGN_TOP_LEFT) return FA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (out_dtype != FA_DTYPE_F32 && out_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (d <= 0) return FA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (in_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+    if (B == 0 || H == 0 || total_q == 0 || max_q == 0) return FA_OK;
+    if (!q || !o || !cu_q || !cu_k) return FA_ERR_INVALID_ARG;
+    if (total_k > 0 && (!k || !v)) return FA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(o, 16) || (k && !aligned(k, 16)) || (v && !aligned(v, 16))) return FA_ERR_INVALID_ARG;
+    if ((lse && !aligned(lse, 4)) || !aligned(cu_q, 4) || !aligned(cu_k, 4)) return FA_ERR_INVALID_ARG;
+    // a key range's byte span must fit the 32-bit range of a buffer resource
+    const int64_t row_bytes = static_cast<int64_t>(H) * d * 2;
+    if (static_cast<int64_t>(max_k) * row_bytes > 0xffffffffLL) return FA_ERR_INVALID_ARG;
+    const bool causal = mask_kind == FA_MASK_CAUSAL;
+    const DecodePlan plan = decode_plan(B, H, max_q, max_k, d);
+    if (plan.ws_bytes > 0) {
+        if (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
+    }
+    const int64_t bh = static_cast<int64_t>(B) * H;
+    const int64_t n_qtiles = (static_cast<int64_t>(max_q) + 127) / 128;
+    const int64_t items = causal ? (n_qtiles + 1) / 2 : n_qtiles;
+    if (bh * items > 0x7fffffff || bh * plan.n_splits > 0x7fffffff || bh * kDecodeMaxRows > 0x7fffffff)
+        return FA_ERR_INVALID_ARG;
+    // outputs must not overlap each other or any input
+    const size_t qb = static_cast<size_t>(total_q) * H * d * 2, kb = static_cast<size_t>(total_k) * H * d * 2;
+    const size_t ob = static_cast<size_t>(total_q) * H * d * (out_dtype == FA_DTYPE_F32 ? 4 : 2);
+    const size_t lb = static_cast<size_t>(total_q) * H * 4;
+    const size_t cb = (static_cast<size_t>(B) + 1) * 4;
+    const void* ins[] = {q, k, v, cu_q, cu_k};
+    const size_t in_sz[] = {qb, kb, kb, cb, cb};
+    const void* outs[] = {o, lse, plan.ws_bytes ? workspace : nullptr};
+    const size_t out_sz[] = {ob, lb, plan.ws_bytes};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i]) continue;
+        for (int j = 0; j < 5; ++j)
+            if (ins[j] && overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 3; ++j)
+            if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_INVALID_ARG;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+    const bool of32 = out_dtype == FA_DTYPE_F32;
+
+    if (plan.g > 0) {
+        fa::DecArgs a;
+        a.q = q;
+        a.k = k;
+        a.v = v;
+        a.o = o;
+        a.lse = lse;
+        a.cu_q = cu_q;
+        a.cu_k = cu_k;
+        a.ws = static_cast<float*>(plan.ws_bytes ? workspace : nullptr);
+        a.B = B;
+        a.H = H;
+        a.total_q = total_q;
+        a.total_k = total_k;
+        a.max_q = max_q;
+        a.max_k = max_k;
+        a.n_splits = plan.n_splits;
+        a.chunk = plan.chunk;
+        a.bottom_right = causal_align == FA_ALIGN_BOTTOM_RIGHT;
+        a.scale_log2 = scale_log2;
+        DecKernel main, merge;
+        if (d == 64) {
+            if (of32) pick_decode<64, true>(plan.g, causal, main, merge);
+            else pick_decode<64, false>(plan.g, causal, main, merge);
+        } else {
+            if (of32) pick_decode<128, true>(plan.g, causal, main, merge);
+            else pick_decode<128, false>(plan.g, causal, main, merge);
+        }
+        hipLaunchKernelGGL(main, dim3(static_cast<unsigned>(bh * plan.n_splits)), dim3(kThreads), 0, st, a);
+        if (!launched_ok()) return FA_ERR_HIP;
+        if (plan.n_splits > 1) {
+            hipLaunchKernelGGL(merge, dim3(static_cast<unsigned>((bh * plan.g + 3) / 4)), dim3(kThreads), 0, st, a);
+            if (!launched_ok()) return FA_ERR_HIP;
+        }
+        return FA_OK;
+    }
+
+    fa::FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.seqlens = nullptr;
+    a.B = B;
+    a.H = H;
+    a.N = 0;
+    a.n_qtiles = static_cast<int>(n_qtiles);
+    a.total_wgs = static_cast<int>(bh * items);
+    a.scale = scale;
+    a.scale_log2 = scale_log2;
+    a.cu_q = cu_q;
+    a.cu_k = cu_k;
+    a.total_q = total_q;
+    a.total_k = total_k;
+    a.max_q = max_q;
+    a.max_k = max_k;
+    a.bottom_right = causal_align == FA_ALIGN_BOTTOM_RIGHT;
+    Kernel kern;
+    if (d == 64) kern = of32 ? pick_varlen<64, true>(causal) : pick_varlen<64, false>(causal);
+    else kern = of32 ? pick_varlen<128, true>(causal) : pick_varlen<128, false>(causal);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(bh * items)), dim3(kThreads), 0, st, a);
+    if (!launched_ok()) return FA_ERR_HIP;
+    return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t fa_fwd_varlen_workspace_size(int B, int H, int max_seqlen_q, int max_seqlen_k, int d) {
+    return decode_plan(B, H, max_seqlen_q, max_seqlen_k, d).ws_bytes;
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int B, int H, int total_q, int total_k, int max_seqlen_q,
+                  int max_seqlen_k, int d, float scale, int mask_kind, int causal_align, void* workspace,
+                  size_t workspace_bytes, int in_dtype, int out_dtype, void* stream) {
+    return varlen_launch(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q,
+                         max_seqlen_k, d, scale, mask_kind, causal_align, workspace, workspace_bytes, in_dtype,
+                         out_dtype, stream);
+}
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int mask_kind,

@@ -49,11 +49,48 @@ struct FwdArgs {
     float* lse;
     const int32_t* seqlens;
     int B, H, N;
-    int n_qtiles;      // ceil(N / BM)
-    int total_wgs;     // B * H * n_qtiles
+    int n_qtiles;      // ceil(N / BM)  (packed sequences: ceil(max_q / BM))
+    int total_wgs;     // B * H * work items per head
     float scale;       // multiplier of the raw dot products
     float scale_log2;  // scale * log2(e)
+    // packed variable-length sequences only (token-major [T, H, d] tensors)
+    const int32_t* cu_q;   // [B + 1] prefix sums of the query lengths
+    const int32_t* cu_k;   // [B + 1] prefix sums of the key lengths
+    int total_q, total_k;  // tokens in the packed query and key tensors
+    int max_q, max_k;      // longest query / key sequence the launch was sized for
+    int bottom_right;      // causal alignment: 1 bottom-right, 0 top-left
 };
+
+// Where the rows of one head of one sequence live, and which keys its queries may see.
+struct SeqGeom {
+    int64_t qbase;  // element offset of query (and output) row 0
+    int64_t kbase;  // element offset of key (and value) row 0
+    int64_t lbase;  // index of row 0's log-sum-exp
+    int Lq;         // query rows
+    int Lk;         // keys
+    int dlt;        // causal mask: key j is visible to query row i iff j <= i + dlt
+    int rse;        // elements between consecutive rows
+};
+
+// Sequence b, head h of a packed batch.  Offsets are clamped into the tensors, so any
+// cu_seqlens values stay memory-safe; lengths are capped at the sizes the launch covers.
+// Bottom-right alignment places the Lq queries at the last Lq of the Lk key positions.
+__device__ __forceinline__ SeqGeom varlen_geom(const FwdArgs& a, int b, int h, int D) {
+    auto clampi = [](int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); };
+    const int qs = clampi(a.cu_q[b], 0, a.total_q);
+    const int qe = clampi(a.cu_q[b + 1], qs, a.total_q);
+    const int ks = clampi(a.cu_k[b], 0, a.total_k);
+    const int ke = clampi(a.cu_k[b + 1], ks, a.total_k);
+    SeqGeom g;
+    g.Lq = qe - qs < a.max_q ? qe - qs : a.max_q;
+    g.Lk = ke - ks < a.max_k ? ke - ks : a.max_k;
+    g.dlt = a.bottom_right ? g.Lk - g.Lq : 0;
+    g.rse = a.H * D;
+    g.qbase = ((int64_t)qs * a.H + h) * D;
+    g.kbase = ((int64_t)ks * a.H + h) * D;
+    g.lbase = (int64_t)h * a.total_q + qs;
+    return g;
+}
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();

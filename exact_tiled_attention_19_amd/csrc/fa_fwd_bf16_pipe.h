@@ -60,9 +60,11 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
-// One query tile (BM rows of head bh) from start to finish; the kernel below runs one or two.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32>
-__device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
+// One query tile (BM rows of head bh) from start to finish; the kernels below run one or two.
+// VL: the rows belong to one sequence of a packed batch described by `sg` (token-major rows,
+// own query and key lengths, causal diagonal offset); otherwise the [B, H, N, d] layout.
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false>
+__device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, const SeqGeom& sg = SeqGeom{}) {
     constexpr int WR = 32 * RB;             // query rows per wave
     constexpr int BM = 4 * WR;              // query rows per workgroup
     constexpr int KC = D / 16;              // k-steps of the S MFMA
@@ -101,16 +103,23 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
 
     const TileCoord tc{bh, qt};
     const int b = tc.bh / a.H;
-    const int N = a.N;
+    const int N = VL ? sg.Lq : a.N;            // query rows of this head
     const int q0 = tc.qt * BM;
     const int qw0 = q0 + wave * WR;          // first query row of this wave
     int qrow[RB];                            // the rows this lane's statistics belong to
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) qrow[rb] = qw0 + 32 * rb + l32;
-    const int64_t base = (int64_t)tc.bh * N * D;
+    const int64_t base = VL ? sg.qbase : (int64_t)tc.bh * N * D;   // query / output rows
+    const int64_t kbase = VL ? sg.kbase : base;                       // key / value rows
+    const int64_t lbase = VL ? sg.lbase : (int64_t)tc.bh * N;         // log-sum-exp entries
+    const int RSE = VL ? sg.rse : D;           // elements between consecutive rows
+    const int RSB = RSE * 2;                   // the same in bytes
+    const int dlt = VL ? sg.dlt : 0;           // causal: key j visible to row i iff j <= i + dlt
 
     int Lk = N;
-    if (PAD) {
+    if (VL) {
+        Lk = sg.Lk;
+    } else if (PAD) {
         const int s = a.seqlens[b];
         Lk = s < 0 ? 0 : (s > N ? N : s);
     }
@@ -118,33 +127,55 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             if (qrow[rb] >= N) continue;
-            if (hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow[rb]] = kNegInf;
+            if (hh == 0 && a.lse) a.lse[lbase + qrow[rb]] = kNegInf;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int d0 = 32 * db + 8 * j + 4 * hh;
-                    if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
-                    else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * D + d0) = u32x2{0u, 0u};
+                    if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * RSE + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * RSE + d0) = u32x2{0u, 0u};
                 }
         }
         return;
     }
 
+    // The causal limits below use the diagonal offset dlt, which is 0 for the [B, H, N, d]
+    // layout; there the original expressions are kept (every term is non-negative).
     int kv_end = Lk;
-    if (CAUSAL) kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
+    if (CAUSAL) {
+        if constexpr (VL) {
+            kv_end = kv_end < q0 + BM + dlt ? kv_end : q0 + BM + dlt;
+            kv_end = kv_end > 0 ? kv_end : 0;
+        } else {
+            kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
+        }
+    }
     const int n_tiles = (kv_end + BN - 1) / BN;
     // tiles this wave computes: under the causal mask the last tiles may lie entirely above
     // this wave's rows and carry no visible key for any of them
     int n_w = n_tiles;
     if (CAUSAL) {
-        const int lim = (qw0 + WR - 1) / BN + 1;
+        int lim;
+        if constexpr (VL) {
+            const int x = qw0 + WR - 1 + dlt;   // last key visible to the wave's last row
+            lim = x < 0 ? 0 : x / BN + 1;
+        } else {
+            lim = (qw0 + WR - 1) / BN + 1;
+        }
         n_w = lim < n_w ? lim : n_w;
     }
+    if (VL && qw0 >= N) n_w = 0;               // a wave past the sequence's last query row
     // tiles [0, n_plain) need no mask for any row of this wave
     int n_plain = Lk / BN;
     if (CAUSAL) {
-        const int c = (qw0 + 1) / BN;           // tiles whose last key <= the wave's first row
+        int c;                                  // tiles whose last key the wave's first row sees
+        if constexpr (VL) {
+            const int x = qw0 + 1 + dlt;
+            c = x < 0 ? 0 : x / BN;
+        } else {
+            c = (qw0 + 1) / BN;
+        }
         n_plain = c < n_plain ? c : n_plain;
     }
 
@@ -152,7 +183,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     bf16x8 qf[RB][KC];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow[rb] < N ? qrow[rb] : N - 1) * D + 8 * hh;
+        const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow[rb] < N ? qrow[rb] : N - 1) * RSE + 8 * hh;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
             qf[rb][c] = *(const bf16x8*)(qp + 16 * c);
@@ -163,23 +194,25 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     // ---- direct-to-LDS tile loads ---------------------------------------------------------
     // Piece r (1 KiB) of a tile holds rows 4r .. 4r+3 (D = 128) or 8r .. 8r+7 (D = 64).  Lane
     // lam writes physical chunk p = 64 r + lam, i.e. row p / CPR, chunk p % CPR, and fetches the
-    // logical chunk that the swizzle maps there.
+    // logical chunk that the swizzle maps there.  The buffer's byte range ends with the last
+    // key row, so rows past it read as zeros (for the packed layout: the last row's end).
+    const int64_t krec = VL ? (int64_t)(Lk - 1) * RSB + ROWB : (int64_t)N * ROWB;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)a.k + base), (short)0, N * ROWB, 0x00020000);
+        (void*)((const uint16_t*)a.k + kbase), (short)0, (int)(uint32_t)krec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)a.v + base), (short)0, N * ROWB, 0x00020000);
+        (void*)((const uint16_t*)a.v + kbase), (short)0, (int)(uint32_t)krec, 0x00020000);
     uint32_t koff[LPW], voff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int p = (i * 4 + wave) * 64 + lane;
         const int row = p / CPR;
         const int pch = p % CPR;
-        koff[i] = row * ROWB + (pch ^ swz_k<D>(row)) * 16;
-        voff[i] = row * ROWB + (pch ^ swz_v<D>(row)) * 16;
+        koff[i] = row * RSB + (pch ^ swz_k<D>(row)) * 16;
+        voff[i] = row * RSB + (pch ^ swz_v<D>(row)) * 16;
     }
     auto load_tile = [&](auto is_v, int tile, int buf_off) __attribute__((always_inline)) {
         constexpr bool IS_V = decltype(is_v)::value;
-        const uint32_t t0 = (uint32_t)tile * (uint32_t)TILEB;
+        const uint32_t t0 = (uint32_t)tile * (uint32_t)(BN * RSB);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
             buffer_load_lds16(IS_V ? vrs : krs, buf(buf_off) + (i * 4 + wave) * 1024,
@@ -204,10 +237,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
     for (int db = 0; db < NDB; ++db) vaddr[db] = vrow * ROWB + (((4 * db + vcl) ^ vswz) * 16) + (l32 & 1) * 8;
 
     auto tile_rsrc = [&](const void* t, int64_t off, int tile) __attribute__((always_inline)) {
-        const int64_t start = (int64_t)tile * TILEB;            // bytes into this head
-        const int64_t left = (int64_t)N * ROWB - start;
+        const int64_t start = (int64_t)tile * BN * RSB;         // bytes into this head
+        const int64_t left = krec - start;
         return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)((const uint16_t*)t + off) + start),
-                                                 (short)0, left > 0 ? (int)left : 0, 0x00020000);
+                                                 (short)0, left > 0 ? (int)(uint32_t)left : 0, 0x00020000);
     };
 
     auto compute_s = [&](f32x16 (&s)[RB][NKB], int kbuf) __attribute__((always_inline)) {
@@ -252,7 +285,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-                        const bool ok = key < Lk && (!CAUSAL || key <= qrow[rb]);
+                        const bool ok = key < Lk && (!CAUSAL || key <= qrow[rb] + dlt);
                         s[rb][kb][r] = ok ? s[rb][kb][r] : kNegInf;
                     }
         }
@@ -369,13 +402,13 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
         // buffer resources starting at tiles j+2 (K) and j+1 (V): the tile offset goes into the
         // scalar base address, so the per-lane offsets need no vector add; the record count
         // shrinks accordingly and keeps rows past N reading as zeros
-        const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, base, j + 2);
-        const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, base, j + 1);
+        const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, kbase, j + 2);
+        const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, kbase, j + 1);
         int vis[RB];   // masked tiles: keys of tile j+1 at offset < vis are visible to the row
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             int lim = Lk;
-            if (CAUSAL) lim = lim < qrow[rb] + 1 ? lim : qrow[rb] + 1;
+            if (CAUSAL) lim = lim < qrow[rb] + 1 + dlt ? lim : qrow[rb] + 1 + dlt;
             vis[rb] = lim - (j + 1) * BN - 4 * hh;
         }
         float rs[RB][2];
@@ -511,8 +544,8 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
         if (j < n_w) {
             fast_body(par_c, masked_c, j);
         } else {
-            const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, base, j + 2);
-            const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, base, j + 1);
+            const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, kbase, j + 2);
+            const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, kbase, j + 1);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
                 buffer_load_lds16(krs_t, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i]);
@@ -566,9 +599,12 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = xor32_sum(l_run[rb]);
-        const float inv_l = 1.0f / l_tot;
+        // packed sequences under the causal mask: a row may see no key at all (bottom-right
+        // alignment with more queries than keys); it gets O = 0 and LSE = -inf
+        const bool none = VL && CAUSAL && !(l_tot > 0.f);
+        const float inv_l = none ? 0.f : 1.0f / l_tot;
         if (qrow[rb] >= N) continue;
-        if (hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow[rb]] = (m_run[rb] + __log2f(l_tot)) * kLn2;
+        if (hh == 0 && a.lse) a.lse[lbase + qrow[rb]] = none ? kNegInf : (m_run[rb] + __log2f(l_tot)) * kLn2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -579,9 +615,9 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt) {
                 const float o2 = acc[rb][db][4 * jj + 2] * inv_l;
                 const float o3 = acc[rb][db][4 * jj + 3] * inv_l;
                 if (OUT_F32) {
-                    *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * D + d0) = f32x4{o0, o1, o2, o3};
+                    *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * RSE + d0) = f32x4{o0, o1, o2, o3};
                 } else {
-                    *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * D + d0) =
+                    *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * RSE + d0) =
                         u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
                 }
             }
@@ -597,6 +633,36 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     if (tp.qt1 >= 0) {
         __syncthreads();   // the first tile's LDS buffers are reused
         pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32>(a, tp.bh, tp.qt1);
+    }
+}
+
+// Packed variable-length sequences ([T, H, d] token-major tensors, per-sequence query and key
+// lengths from prefix sums).  The launch covers the longest query sequence; work item `it` of
+// (sequence, head) takes tile `it` (or, under the causal mask, the pair (it, n-1-it) of the
+// sequence's own n tiles) and items past the sequence's tiles exit at once.
+template <int D, int BN, int RB, bool CAUSAL, bool OUT_F32>
+__global__ void __launch_bounds__(256, 2) fa_fwd_bf16_varlen_kernel(FwdArgs a) {
+    constexpr int BM = 128 * RB;
+    const int logical = xcd_remap(blockIdx.x, a.total_wgs);
+    const int per = items_per_head(a.n_qtiles, CAUSAL);
+    const int bh = logical / per;
+    const int it = logical - bh * per;
+    const int b = bh / a.H;
+    const SeqGeom sg = varlen_geom(a, b, bh - b * a.H, D);
+    const int n = (sg.Lq + BM - 1) / BM;
+    int qt0, qt1 = -1;
+    if (CAUSAL) {
+        if (it >= (n + 1) / 2) return;
+        qt0 = n - 1 - it;
+        if (it < qt0) qt1 = it;
+    } else {
+        if (it >= n) return;
+        qt0 = it;
+    }
+    pipe_tile<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt0, sg);
+    if (qt1 >= 0) {
+        __syncthreads();
+        pipe_tile<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt1, sg);
     }
 }
 

@@ -126,6 +126,68 @@ def make_inputs(w: Workload, mask_kind: Optional[int] = None, sample_rows: Optio
     return Inputs(q, k, v, seqlens, rows, w.scale)
 
 
+# ---- packed variable-length workloads --------------------------------------------------------
+# The pages name decoding, unequal query/key lengths and packed sequences as cases whose key
+# visibility must be settled explicitly, but quote no sizes for them; these stand-ins reuse the
+# key/value shapes and token budgets of the named workloads above.
+@dataclasses.dataclass(frozen=True)
+class PackedWorkload:
+    name: str
+    H: int
+    d: int
+    lq: tuple                 # query length of every sequence
+    lk: tuple                 # key length of every sequence
+    causal: bool
+    align: str                # "bottom_right" or "top_left"
+    seed: int
+    sample_seqs: Optional[int] = None   # sequences the oracle checks at full size (None = all)
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return scale_for(self.d)
+
+
+def draw_lengths(seed: int, n: int, lo: int, hi: int) -> tuple:
+    """n sequence lengths, integers uniform on [lo, hi], from their own generator."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return tuple(int(x) for x in torch.randint(lo, hi + 1, (n,), generator=g))
+
+
+_MIX = draw_lengths(7, 16, 256, 4096)
+PACKED = {
+    "decode_c2kv": PackedWorkload("decode_c2kv", 16, 128, (1,) * 4, (8192,) * 4, True, "bottom_right", seed=20,
+                                  description="one new query row per sequence against the c2 key/value shape "
+                                              "(B=4, H=16, 8192 keys, d=128)"),
+    "decode_c4kv": PackedWorkload("decode_c4kv", 8, 128, (1,), (131072,), True, "bottom_right", seed=21,
+                                  description="one new query row against the c4 key/value shape "
+                                              "(H=8, 131072 keys, d=128)"),
+    "chunked_prefill": PackedWorkload("chunked_prefill", 16, 128, (512,) * 4, (8192,) * 4, True, "bottom_right",
+                                      seed=22, sample_seqs=1,
+                                      description="the last 512 positions of four 8192-token sequences "
+                                                  "(H=16, d=128), bottom-right causal"),
+    "varlen_mix": PackedWorkload("varlen_mix", 16, 128, _MIX, _MIX, True, "bottom_right", seed=23, sample_seqs=2,
+                                 description="16 packed causal sequences, lengths uniform on [256, 4096] "
+                                             f"({sum(_MIX)} tokens, H=16, d=128)"),
+}
+
+
+def random_packed(lq, lk, H: int, d: int, dtype: torch.dtype, seed: int, qk_gain: float = 1.0):
+    """Token-major packed inputs: Q [sum(lq), H, d], K and V [sum(lk), H, d] (standard normals,
+    Q and K times ``qk_gain``, cast to ``dtype``) and the int32 prefix sums of the lengths."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    Tq, Tk = int(sum(lq)), int(sum(lk))
+    q = torch.randn(Tq, H, d, generator=g, dtype=torch.float32)
+    k = torch.randn(Tk, H, d, generator=g, dtype=torch.float32)
+    v = torch.randn(Tk, H, d, generator=g, dtype=torch.float32)
+    if qk_gain != 1.0:
+        q.mul_(qk_gain)
+        k.mul_(qk_gain)
+    cu_q = torch.tensor([0] + [int(x) for x in torch.cumsum(torch.tensor(lq, dtype=torch.int64), 0)], dtype=torch.int32)
+    cu_k = torch.tensor([0] + [int(x) for x in torch.cumsum(torch.tensor(lk, dtype=torch.int64), 0)], dtype=torch.int32)
+    return q.to(dtype), k.to(dtype), v.to(dtype), cu_q, cu_k
+
+
 def scale_for(d: int) -> float:
     """1/sqrt(d) rounded to float32, the value passed across the C ABI."""
     return float(torch.tensor(1.0 / math.sqrt(d), dtype=torch.float32).item())

@@ -36,13 +36,14 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define FA_VERSION 10100 /* major*10000 + minor*100 + patch */
+#define FA_VERSION 10200 /* major*10000 + minor*100 + patch */
 
 typedef enum {
     FA_OK = 0,
@@ -55,6 +56,8 @@ typedef enum {
 
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_KEY_PADDING = 2 };
 enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 };
+/* Causal alignment of fa_fwd_varlen (see there). */
+enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 };
 
 /*
  * fa_fwd -- the fused forward pass.
@@ -123,6 +126,66 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dout, float* delta, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
            int in_dtype, int grad_dtype, void* stream);
+
+/*
+ * fa_fwd_varlen -- the forward pass over a packed batch of sequences with their own query and
+ * key lengths: unequal query and key counts, variable-length (packed) batches and decoding
+ * (one or a few new query rows against a long key range).  The cswork.org page warns that
+ * these cases change which keys a query may see (section "Does subtracting the maximum solve
+ * every numerical issue?") and separates prefill from single-token decoding (closing benchmark
+ * section); the visibility rule is therefore explicit here:
+ *
+ *   Sequence b owns query tokens cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 (Lq of them) and key /
+ *   value tokens cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 (Lk of them).  Sequences never see each
+ *   other's keys.  Without a mask every key of the sequence is visible.  Under FA_MASK_CAUSAL,
+ *   query row i (0-based within its sequence) sees key j iff j <= i + delta, with
+ *     causal_align == FA_ALIGN_BOTTOM_RIGHT: delta = Lk - Lq (the queries are the last Lq of
+ *                     the Lk positions: decoding, chunked prefill);
+ *     causal_align == FA_ALIGN_TOP_LEFT:     delta = 0 (query i and key i share a position).
+ *   The two agree when Lq == Lk.  A row that sees no key (bottom-right with Lq > Lk, or Lk == 0)
+ *   gets O = 0 and LSE = -inf.
+ *
+ *   q, o      [total_q, H, d] token-major (d fastest, then heads), 16-byte aligned; q of
+ *             `in_dtype`, o of `out_dtype`, written.  o must not overlap any input.
+ *   k, v      [total_k, H, d] of `in_dtype`, 16-byte aligned (may be NULL when total_k == 0).
+ *   lse       [H, total_q] float32, 4-byte aligned, natural-log log-sum-exp; NULL: not stored.
+ *   cu_seqlens_q, cu_seqlens_k   device int32[B + 1] prefix sums of the lengths: first entry 0,
+ *             non-decreasing, last entry <= total.  Each length must be <= max_seqlen_q /
+ *             max_seqlen_k.  (Memory safety does not depend on this: entries are clamped into
+ *             the tensors and lengths to the maxima, rows past max_seqlen_q are then not
+ *             written and keys past max_seqlen_k are ignored.)
+ *   B, H      sequences and heads.  max_seqlen_q, max_seqlen_k: the longest query and key
+ *             sequence (>= 0); they size the launch.  max_seqlen_k * H * d * 2 must be < 2^32.
+ *   d, scale  as for fa_fwd.  mask_kind: FA_MASK_NONE or FA_MASK_CAUSAL (key lengths come
+ *             from cu_seqlens_k, so FA_MASK_KEY_PADDING is invalid here).
+ *   causal_align   FA_ALIGN_BOTTOM_RIGHT or FA_ALIGN_TOP_LEFT; required (validated) even
+ *             without the causal mask, which ignores it.
+ *   workspace, workspace_bytes   device scratch owned by the caller, 16-byte aligned, of at
+ *             least fa_fwd_varlen_workspace_size(B, H, max_seqlen_q, max_seqlen_k, d) bytes
+ *             (NULL / 0 when that size is 0).  It must not overlap any other argument; its
+ *             contents on entry do not matter and on return are unspecified.
+ *   in_dtype, out_dtype   (BF16, BF16) or (BF16, F32), d in {64, 128}.
+ *   stream    hipStream_t to enqueue on (NULL = default stream).
+ *
+ * Kernels: when max_seqlen_q <= 4 (decoding shapes) the keys of every (sequence, head) are cut
+ * into ranges processed by separate workgroups with fp32 vector arithmetic (the work is bound
+ * by the K/V stream), and a second kernel merges the ranges' running statistics; otherwise the
+ * tiled MFMA kernel of fa_fwd runs on the packed layout.  No atomics: results are identical
+ * from run to run.  Validation is done on the host before any HIP call; B, H, total_q or
+ * max_seqlen_q equal to 0 is a no-op.  Returns an fa_status.
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                  int B, int H, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                  int d, float scale, int mask_kind, int causal_align,
+                  void* workspace, size_t workspace_bytes,
+                  int in_dtype, int out_dtype, void* stream);
+
+/*
+ * Bytes of workspace fa_fwd_varlen needs for these sizes (0: none).  A pure function of its
+ * arguments; 0 for sizes fa_fwd_varlen would reject.
+ */
+size_t fa_fwd_varlen_workspace_size(int B, int H, int max_seqlen_q, int max_seqlen_k, int d);
 
 /* Number of kernel variants fa_fwd_variant accepts (variants are 0 .. count-1). */
 int fa_variant_count(void);

@@ -30,7 +30,7 @@ P4 = 0xC0000000
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_expected_api():
@@ -155,6 +155,76 @@ def test_bwd_unsupported_rejected_on_host(name):
 
 def test_bwd_empty_problem_is_a_noop():
     assert fa.fa_bwd(*([None] * 10), 0, 4, 16, 64, 0.125, 1, None, BF16, F32, None) == fa.FA_OK
+
+
+# ---- packed variable-length entry point --------------------------------------------------------
+VQ, VK, VV, VO = 0x10000, 0x40000000, 0x80000000, 0xC0000000
+VCQ, VCK, VL, VW = 0x100000000, 0x100001000, 0x140000000, 0x180000000
+
+
+def varlen_call(q=VQ, k=VK, v=VV, o=VO, lse=VL, cu_q=VCQ, cu_k=VCK, B=2, H=2, total_q=64, total_k=64, max_q=32,
+                max_k=32, d=64, scale=0.125, mask=0, align=fa.FA_ALIGN_BOTTOM_RIGHT, ws=None, ws_bytes=0, ind=BF16,
+                outd=BF16):
+    return fa.fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, max_k, d, scale, mask, align,
+                            ws, ws_bytes, ind, outd, None)
+
+
+DEC = dict(max_q=1, total_q=2, max_k=8192)   # decoding shape: needs a workspace for these sizes
+VARLEN_INVALID = {
+    "null q": dict(q=None), "null o": dict(o=None), "null cu_q": dict(cu_q=None), "null cu_k": dict(cu_k=None),
+    "null k with keys": dict(k=None), "null v with keys": dict(v=None),
+    "negative B": dict(B=-1), "negative H": dict(H=-1), "negative total_q": dict(total_q=-1),
+    "negative total_k": dict(total_k=-5), "negative max_q": dict(max_q=-1), "negative max_k": dict(max_k=-1),
+    "key padding bit": dict(mask=fa.FA_MASK_KEY_PADDING), "causal and padding": dict(mask=3), "mask -1": dict(mask=-1),
+    "alignment 2": dict(align=2), "alignment -1": dict(align=-1, mask=1),
+    "nan scale": dict(scale=float("nan")), "negative scale": dict(scale=-1.0),
+    "misaligned q": dict(q=VQ + 2), "misaligned k": dict(k=VK + 8), "misaligned o": dict(o=VO + 4),
+    "misaligned lse": dict(lse=VL + 2), "misaligned cu_q": dict(cu_q=VCQ + 2), "misaligned cu_k": dict(cu_k=VCK + 1),
+    "bad in dtype": dict(ind=9), "bad out dtype": dict(outd=3), "d zero": dict(d=0),
+    "o aliases q": dict(o=VQ), "o overlaps v": dict(o=VV + 32), "lse inside o": dict(lse=VO + 64),
+    "lse overlaps cu_q": dict(lse=VCQ), "o overlaps cu_k": dict(o=VCK - 64),
+    "key range beyond 32-bit buffer": dict(H=64, d=128, max_k=300000),
+    "decode without workspace": dict(DEC),
+    "decode workspace too small": dict(DEC, ws=VW, ws_bytes=16),
+    "decode workspace misaligned": dict(DEC, ws=VW + 8, ws_bytes=1 << 24),
+    "decode workspace overlaps o": dict(DEC, ws=VO, ws_bytes=1 << 24),
+}
+VARLEN_UNSUPPORTED = {"d 96": dict(d=96), "d 256": dict(d=256), "f32 inputs": dict(ind=F32, outd=F32)}
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_INVALID))
+def test_varlen_invalid_argument_rejected_on_host(name):
+    assert varlen_call(**VARLEN_INVALID[name]) == fa.FA_ERR_INVALID_ARG, name
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_UNSUPPORTED))
+def test_varlen_unsupported_rejected_on_host(name):
+    assert varlen_call(**VARLEN_UNSUPPORTED[name]) == fa.FA_ERR_UNSUPPORTED, name
+
+
+@pytest.mark.parametrize("dims", [dict(B=0), dict(H=0), dict(total_q=0), dict(max_q=0)])
+def test_varlen_empty_problem_is_a_noop(dims):
+    args = dict(q=None, k=None, v=None, o=None, lse=None, cu_q=None, cu_k=None)
+    args.update(dims)
+    assert varlen_call(**args) == fa.FA_OK
+
+
+def test_varlen_workspace_size():
+    """Workspace only for decoding shapes (<= 4 query rows) whose key ranges are split; its size
+    is B*H*ranges*rows*(d+2)*4 bytes, a pure function of the sizes."""
+    ws = fa.varlen_workspace_size
+    assert ws(4, 16, 5, 8192, 128) == 0                 # prefill shape: tile kernel
+    assert ws(64, 64, 1, 8192, 128) == 0                # 4096 heads fill the chip: one range
+    assert ws(4, 16, 1, 200, 128) == 0                  # too few keys to split
+    assert ws(-1, 16, 1, 8192, 128) == 0 and ws(4, 16, 1, 8192, 96) == 0
+    for B, H, mq, mk, d in [(4, 16, 1, 8192, 128), (1, 8, 1, 131072, 128), (2, 3, 4, 5000, 64), (1, 1, 2, 1 << 20, 64)]:
+        g = 1 if mq == 1 else 4
+        n = ws(B, H, mq, mk, d)
+        unit = B * H * g * (d + 2) * 4
+        assert n > 0 and n % unit == 0, (B, H, mq, mk, d, n)
+        S = n // unit
+        assert 2 <= S <= max(2, -(-2048 // (B * H))) and S <= -(-mk // 256), S
+        assert ws(B, H, mq, mk, d) == n                 # deterministic
 
 
 def test_python_forward_rejects_host_tensors():
