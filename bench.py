@@ -13,6 +13,11 @@ resident in device memory.  Prints one JSON line:
   cpu_baseline  the fp64 CPU oracle timed on this host on a bounded sample of the same
              workload (seed-chosen query rows of every head), scaled to TFLOP/s.
 
+Packed variable-length workloads (--workload decode_c2kv | decode_c4kv | chunked_prefill |
+varlen_mix) time fa_fwd_varlen instead: decoding steps are bound by the K/V stream and are
+reported in GB/s against the HBM peak; packed prefill in TFLOP/s counting 4*d FLOP per visible
+(query, key) pair.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
        python bench.py --calibrate-copy      (a plain conversion copy of known size, for scaling
                                               the FETCH_SIZE / WRITE_SIZE counters to bytes)
@@ -22,6 +27,7 @@ from __future__ import annotations
 
 import argparse
 import dataclasses
+import glob
 import hashlib
 import json
 import math
@@ -36,8 +42,9 @@ METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4k–128k, d=64/128, 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_bf16_pipe_c2_causal_traffic.txt")
-KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h"]
+TRAFFIC_FILES = os.path.join(ROOT, "profiles", "*_traffic.txt")
+KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h",
+                  "fa_decode_bf16.h"]
 
 
 def kernel_source_hash() -> str:
@@ -59,22 +66,144 @@ def counted_flops(B, H, N, d, causal) -> float:
 
 
 def recorded_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when the
-    summary is absent, is for another workload, or predates the current kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    vals = {}
-    with open(TRAFFIC_FILE) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                key, val = line.split(":", 1)
-                vals[key.strip()] = val.strip()
-    if vals.get("workload") != workload or vals.get("kernel_source_sha256_16") != kernel_source_hash():
-        return None
-    try:
-        return float(vals["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    """HBM bytes per launch from a committed rocprofv3 counter summary for this workload, or
+    None when there is none or it predates the current kernel sources."""
+    for path in sorted(glob.glob(TRAFFIC_FILES)):
+        vals = {}
+        with open(path) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    key, val = line.split(":", 1)
+                    vals[key.strip()] = val.strip()
+        if vals.get("workload") != workload or vals.get("kernel_source_sha256_16") != kernel_source_hash():
+            continue
+        try:
+            return float(vals["hbm_bytes_per_launch"])
+        except (KeyError, ValueError):
+            continue
+    return None
+
+
+def visible_pairs(lq, lk, causal: bool, align: str) -> int:
+    """(query, key) pairs the mask lets through, summed over the packed sequences."""
+    total = 0
+    for a, b in zip(lq, lk):
+        if not causal:
+            total += a * b
+            continue
+        dlt = b - a if align == "bottom_right" else 0
+        for i in range(a):   # row i sees keys 0 .. min(b - 1, i + dlt)
+            total += max(0, min(b, i + dlt + 1))
+    return total
+
+
+def time_steps(step, steps: int, warmup: int, dev):
+    """W untimed steps, then K timed ones; returns (wall seconds, mean per-step HIP-event seconds)."""
+    import torch
+    print(f"[bench] warmup {warmup}", file=sys.stderr, flush=True)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    print(f"[bench] timing {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    return wall, sum(launch_ms) / len(launch_ms) / 1e3
+
+
+def bench_packed(args, w) -> int:
+    """fa_fwd_varlen on a packed workload: decoding shapes against the HBM peak (bytes of Q, K,
+    V read and O, LSE written once), packed prefill against the bf16 MFMA peak."""
+    import torch
+    import exact_tiled_attention_19_amd as fa
+    from exact_tiled_attention_19_amd import workloads as W
+    dev = torch.device("cuda", 0)
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    qh, kh, vh, cqh, ckh = W.random_packed(w.lq, w.lk, w.H, w.d, torch.bfloat16, w.seed)
+    q, k, v, cu_q, cu_k = (t.to(dev) for t in (qh, kh, vh, cqh, ckh))
+    mq, mk = max(w.lq), max(w.lk)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.H, q.shape[0]), dtype=torch.float32, device=dev)
+    nws = fa.varlen_workspace_size(len(w.lq), w.H, mq, mk, w.d)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev) if nws else None
+    torch.cuda.synchronize()
+
+    def step():
+        fa.forward_varlen(q, k, v, cu_q, cu_k, mq, mk, scale=w.scale, causal=w.causal, align=w.align,
+                          out=o, lse_out=lse, workspace=ws)
+
+    wall, avg_launch_s = time_steps(step, args.steps, args.warmup, dev)
+    decode = mq <= 4
+    Tq, Tk = sum(w.lq), sum(w.lk)
+    nbytes = w.H * w.d * 2 * (Tq + 2 * Tk) + w.H * w.d * 2 * Tq + 4 * w.H * Tq
+    flops = 4.0 * w.d * w.H * visible_pairs(w.lq, w.lk, w.causal, w.align)
+    mask_name = f"causal {w.align.replace('_', '-')}" if w.causal else "none"
+    workload_id = f"{w.name}:{'causal-' + w.align if w.causal else 'none'}:bf16-out"
+    if decode:
+        metric, unit, bound, peak = ("attention decode GB/s (Q, K, V read and O, LSE written once), 1 GPU",
+                                     "GB/s", "hbm", PEAK_HBM_GBS)
+        value = nbytes / (wall / args.steps) / 1e9
+        achieved = nbytes / avg_launch_s / 1e9
+    else:
+        metric, unit, bound, peak = ("attention fwd TFLOP/s, packed variable-length sequences (4*d FLOP per "
+                                     "visible query-key pair), 1 GPU", "TFLOP/s", "mfma", PEAK_BF16_TFLOPS)
+        value = flops / (wall / args.steps) / 1e12
+        achieved = flops / avg_launch_s / 1e12
+    res = {
+        "metric": metric, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normal Q, K, V of the workload's packed shape; no dataset)",
+        "config": {
+            "workload": f"{w.name}: {w.description}; {mask_name} mask; bf16 in, bf16 out, fp32 LSE",
+            "sequences": len(w.lq), "H": w.H, "d": w.d, "tokens_q": Tq, "tokens_k": Tk,
+            "max_seqlen_q": mq, "max_seqlen_k": mk, "kernel": "decode (split keys + merge)" if decode else "tile",
+            "workspace_bytes": nws, "flop_per_step": flops, "compulsory_bytes_per_step": nbytes,
+        },
+        "roofline": {
+            "bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 5), "traffic": recorded_traffic(workload_id),
+            "kernel_avg_ms": round(avg_launch_s * 1e3, 5),
+        },
+    }
+    if decode and nws:
+        res["roofline"]["note"] = "HIP events bracket both kernels of a step (the key ranges and their merge)"
+    if not args.no_cpu_baseline:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                          default=1)
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        # bounded sample: whole decoding steps, or the first sequences of a packed prefill batch
+        nseq = len(w.lq) if decode else max(1, min(len(w.lq), 2))
+        sq, sk = list(w.lq[:nseq]), list(w.lk[:nseq])
+        qs, ks = sum(sq), sum(sk)
+        print(f"[bench] timing the fp64 oracle on {nseq} sequence(s)", file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        oracle.attention_varlen_ref(qh[:qs], kh[:ks], vh[:ks], [0] + list(torch.cumsum(torch.tensor(sq), 0).tolist()),
+                                    [0] + list(torch.cumsum(torch.tensor(sk), 0).tolist()), w.scale,
+                                    causal=w.causal, align=w.align)
+        dt = time.perf_counter() - t0
+        if decode:
+            sb = w.H * w.d * 2 * (qs + 2 * ks) + w.H * w.d * 2 * qs + 4 * w.H * qs
+            cv = sb / dt / 1e9
+        else:
+            cv = 4.0 * w.d * w.H * visible_pairs(sq, sk, w.causal, w.align) / dt / 1e12
+        res["cpu_baseline"] = {"value": round(cv, 6), "unit": unit, "cores": int(threads), "kind": "oracle",
+                               "sample": f"{nseq} of the {len(w.lq)} sequences, all heads, fp64 numpy, "
+                                         f"{dt:.1f} s wall"}
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def cpu_baseline(w, x, rows_per_head: int):
@@ -134,8 +263,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed launches first: the shader clock settles over the first ~100 ms")
     ap.add_argument("--workload", default="c2",
-                    help="c0..c4 (default c2, the roofline workload), or a short-sequence HBM probe "
-                         "bw<N>d<d> with N in 128/256/512 and d in 64/128")
+                    help="c0..c4 (default c2, the roofline workload), a short-sequence HBM probe "
+                         "bw<N>d<d> with N in 128/256/512 and d in 64/128, or a packed workload "
+                         "(decode_c2kv, decode_c4kv, chunked_prefill, varlen_mix)")
     ap.add_argument("--mask", type=int, default=None, help="override the workload's mask bits")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--variant", type=int, default=0)
@@ -167,6 +297,8 @@ def main() -> int:
     if args.calibrate_copy:
         return calibrate_copy(args.steps)
     fa.load_library()
+    if args.workload in W.PACKED:
+        return bench_packed(args, W.PACKED[args.workload])
     probe = args.workload in W.PROBES
     w = W.PROBES[args.workload] if probe else W.WORKLOADS[args.workload]
     mask = w.mask_kinds[0] if args.mask is None else args.mask

@@ -249,6 +249,9 @@ constexpr int kDecodeMaxRows = 4;
 // Workgroups the decoding kernel aims for (8 per CU), and the fewest keys per range.
 constexpr int64_t kDecodeTargetWgs = 2048;
 constexpr int64_t kDecodeMinKeys = 256;
+// Tile kernel on packed sequences: fewest tiles (over all sequences and heads, counted at the
+// longest query sequence) for which causal tiles are paired.
+constexpr int64_t kPairMinTiles = 4096;
 
 struct DecodePlan {
     int g;            // query rows per sequence the kernel handles (0: not a decoding shape)
@@ -273,6 +276,7 @@ DecodePlan decode_plan(int B, int H, int max_q, int max_k, int d) {
     if (chunk < step) chunk = step;
     S = (max_k + chunk - 1) / chunk;
     if (S < 1) S = 1;
+    if (S > fa::kDecodeMaxSplits) return DecodePlan{0, 1, 0, 0};   // not reached: S <= kDecodeTargetWgs
     p.n_splits = static_cast<int>(S);
     p.chunk = static_cast<int>(chunk);
     p.ws_bytes = S > 1 ? static_cast<size_t>(bh) * S * p.g * (d + 2) * sizeof(float) : 0;
@@ -327,7 +331,10 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
     }
     const int64_t bh = static_cast<int64_t>(B) * H;
     const int64_t n_qtiles = (static_cast<int64_t>(max_q) + 127) / 128;
-    const int64_t items = causal ? (n_qtiles + 1) / 2 : n_qtiles;
+    // causal tiles are paired (equal work per item) only when the pairs still fill the chip
+    // several times over; otherwise every tile is its own work item
+    const bool pair = causal && bh * n_qtiles >= kPairMinTiles;
+    const int64_t items = pair ? (n_qtiles + 1) / 2 : n_qtiles;
     if (bh * items > 0x7fffffff || bh * plan.n_splits > 0x7fffffff || bh * kDecodeMaxRows > 0x7fffffff)
         return FA_ERR_INVALID_ARG;
     // outputs must not overlap each other or any input
@@ -381,7 +388,8 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
         hipLaunchKernelGGL(main, dim3(static_cast<unsigned>(bh * plan.n_splits)), dim3(kThreads), 0, st, a);
         if (!launched_ok()) return FA_ERR_HIP;
         if (plan.n_splits > 1) {
-            hipLaunchKernelGGL(merge, dim3(static_cast<unsigned>((bh * plan.g + 3) / 4)), dim3(kThreads), 0, st, a);
+            const int64_t merge_wgs = bh * plan.g * (d / fa::kMergeCols);
+            hipLaunchKernelGGL(merge, dim3(static_cast<unsigned>(merge_wgs)), dim3(kThreads), 0, st, a);
             if (!launched_ok()) return FA_ERR_HIP;
         }
         return FA_OK;
@@ -408,6 +416,7 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
     a.max_q = max_q;
     a.max_k = max_k;
     a.bottom_right = causal_align == FA_ALIGN_BOTTOM_RIGHT;
+    a.pair = pair ? 1 : 0;
     Kernel kern;
     if (d == 64) kern = of32 ? pick_varlen<64, true>(causal) : pick_varlen<64, false>(causal);
     else kern = of32 ? pick_varlen<128, true>(causal) : pick_varlen<128, false>(causal);

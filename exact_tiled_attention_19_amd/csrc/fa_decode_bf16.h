@@ -238,13 +238,28 @@ __global__ void __launch_bounds__(256) fa_decode_kernel(DecArgs a) {
     }
 }
 
-// Combine the key ranges of fa_decode_kernel: one wave per (sequence, head, query row).
+// Most key ranges one (sequence, head) is cut into (the host caps the split count here).
+constexpr int kDecodeMaxSplits = 2048;
+
+// Combine the key ranges of fa_decode_kernel.  One workgroup per (sequence, head, query row,
+// slice of MCW output columns): all 256 threads first find the largest range maximum M and
+// the weights exp2(m_r - M) (kept in LDS) and the total l; then 256 / MCW groups of threads
+// each sum a share of the ranges for the slice's columns, so the partial states are read with
+// many loads in flight instead of one range after another.
+constexpr int kMergeCols = 16;
+
 template <int D, int G, bool OUT_F32>
 __global__ void __launch_bounds__(256) fa_decode_merge_kernel(DecArgs a) {
-    constexpr int EPL = D / 64;            // columns per lane
-    const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (item >= a.B * a.H * G) return;     // uniform per wave
+    constexpr int MCW = kMergeCols;
+    constexpr int NCS = D / MCW;           // column slices per row
+    constexpr int NSG = 256 / MCW;         // range groups
+    __shared__ float wsh[kDecodeMaxSplits];
+    __shared__ float red[4];
+    __shared__ float part[NSG][MCW];
+
+    const int tid = threadIdx.x;
+    const int item = blockIdx.x / NCS;
+    const int cs = blockIdx.x - item * NCS;
     const int bh = item / G;
     const int g = item - bh * G;
     const int b = bh / a.H;
@@ -254,33 +269,58 @@ __global__ void __launch_bounds__(256) fa_decode_merge_kernel(DecArgs a) {
     const int qe = clampi(a.cu_q[b + 1], qs, a.total_q);
     int Lq = qe - qs < a.max_q ? qe - qs : a.max_q;
     Lq = Lq < G ? Lq : G;
-    if (g >= Lq) return;
+    if (g >= Lq) return;                   // uniform over the workgroup
 
     const int S = a.n_splits;
-    const float* accp = a.ws + ((int64_t)bh * S * G + g) * D;
-    const float* ml = a.ws + (int64_t)a.B * a.H * S * G * D + ((int64_t)bh * S * G + g) * 2;
-    float M = kNegInf;
-    for (int s = 0; s < S; ++s) M = __builtin_elementwise_maximum(M, ml[(int64_t)s * G * 2]);
-    float L = 0.f, A[EPL];
+    const float* ml = a.ws + (int64_t)a.B * a.H * S * G * D;
+    auto m_of = [&](int s) { return ml[2 * (((int64_t)bh * S + s) * G + g)]; };
+    auto l_of = [&](int s) { return ml[2 * (((int64_t)bh * S + s) * G + g) + 1]; };
+    auto block_reduce = [&](float x, bool is_max) {
 #pragma unroll
-    for (int t = 0; t < EPL; ++t) A[t] = 0.f;
-    if (M != kNegInf) {
-        for (int s = 0; s < S; ++s) {
-            const float w = fast_exp2(ml[(int64_t)s * G * 2] - M);
-            L = fmaf(ml[(int64_t)s * G * 2 + 1], w, L);
-#pragma unroll
-            for (int t = 0; t < EPL; ++t) A[t] = fmaf(accp[(int64_t)s * G * D + lane + 64 * t], w, A[t]);
+        for (int o = 32; o >= 1; o >>= 1) {
+            const float y = __shfl_xor(x, o);
+            x = is_max ? __builtin_elementwise_maximum(x, y) : x + y;
         }
+        if ((tid & 63) == 0) red[tid >> 6] = x;
+        __syncthreads();
+        const float r = is_max ? __builtin_elementwise_maximum(__builtin_elementwise_maximum(red[0], red[1]),
+                                                               __builtin_elementwise_maximum(red[2], red[3]))
+                               : (red[0] + red[1]) + (red[2] + red[3]);
+        __syncthreads();                   // red is reused
+        return r;
+    };
+
+    float mloc = kNegInf;
+    for (int s = tid; s < S; s += 256) mloc = __builtin_elementwise_maximum(mloc, m_of(s));
+    const float M = block_reduce(mloc, true);
+    float lloc = 0.f;
+    for (int s = tid; s < S; s += 256) {
+        const float w = M == kNegInf ? 0.f : fast_exp2(m_of(s) - M);   // empty ranges weigh 0
+        wsh[s] = w;
+        lloc = fmaf(l_of(s), w, lloc);
     }
-    const bool none = !(L > 0.f);
-    const int64_t row = (int64_t)(qs + g) * a.H + h;
+    const float L = block_reduce(lloc, false);   // its barriers also publish wsh
+
+    const int c = tid % MCW;
+    const int sg = tid / MCW;
+    const int col = cs * MCW + c;
+    const float* accp = a.ws + ((int64_t)bh * S * G + g) * D + col;
+    float A = 0.f;
+#pragma unroll 8
+    for (int s = sg; s < S; s += NSG) A = fmaf(wsh[s], accp[(int64_t)s * G * D], A);
+    part[sg][c] = A;
+    __syncthreads();
+    if (tid < MCW) {
+        float t = 0.f;
 #pragma unroll
-    for (int t = 0; t < EPL; ++t) {
-        const float o = none ? 0.f : A[t] / L;
-        if (OUT_F32) ((float*)a.o)[row * D + lane + 64 * t] = o;
-        else ((__bf16*)a.o)[row * D + lane + 64 * t] = (__bf16)o;
+        for (int r = 0; r < NSG; ++r) t += part[r][tid];
+        const bool none = !(L > 0.f);
+        const int64_t row = (int64_t)(qs + g) * a.H + h;
+        const float o = none ? 0.f : t / L;
+        if (OUT_F32) ((float*)a.o)[row * D + col] = o;
+        else ((__bf16*)a.o)[row * D + col] = (__bf16)o;
+        if (cs == 0 && tid == 0 && a.lse) a.lse[(int64_t)h * a.total_q + qs + g] = none ? kNegInf : (M + __log2f(L)) * kLn2;
     }
-    if (lane == 0 && a.lse) a.lse[(int64_t)h * a.total_q + qs + g] = none ? kNegInf : (M + __log2f(L)) * kLn2;
 }
 
 }  // namespace fa

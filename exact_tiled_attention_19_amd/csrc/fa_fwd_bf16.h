@@ -59,6 +59,7 @@ struct FwdArgs {
     int total_q, total_k;  // tokens in the packed query and key tensors
     int max_q, max_k;      // longest query / key sequence the launch was sized for
     int bottom_right;      // causal alignment: 1 bottom-right, 0 top-left
+    int pair;              // causal: a work item is a tile pair (t, n-1-t) of one sequence
 };
 
 // Where the rows of one head of one sequence live, and which keys its queries may see.

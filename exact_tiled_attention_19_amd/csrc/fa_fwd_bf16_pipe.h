@@ -23,6 +23,12 @@
 //     With a float32 output (P = P_hi + P_lo, two bf16 products) the shift is raised only when
 //     a row's tile maximum exceeds it by more than 8 (log2 units), which skips most rescales.
 //     Numerator and denominator share every shift, so the result is unchanged.
+//   * Probability precision.  The value product takes P as one bf16 term (relative rounding
+//     up to 2^-9) except where that error is not averaged away: a float32 output always uses
+//     P_hi + P_lo, and with a bf16 output so do the masked tiles of a wave with a row that sees
+//     fewer than one tile of keys (all of whose keys lie in masked tiles).  For such a row one
+//     rounded probability could otherwise move the output by a few 1e-3 on top of the output's
+//     own bf16 rounding; with a tile of keys or more the rounding errors average out.
 //   * Direct-to-LDS loads.  K/V tiles move global -> LDS with buffer_load_dwordx4 ... lds.
 //     Each instruction fills 1 KiB of LDS in lane order, so the bank-conflict-free layout is an
 //     XOR swizzle of the 16-byte chunks of each row, realised by choosing which global chunk
@@ -60,10 +66,22 @@ __device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
 
+// The four K/V tile buffers in LDS: one object per (size, id), shared by every instantiation of
+// pipe_tile with that tile size, so a kernel that runs two instantiations does not double its
+// LDS.  Distinct objects (not offsets into one array) let the compiler see that an outstanding
+// global->LDS load into one buffer does not alias LDS reads from another.
+template <int TILEB, int ID>
+__device__ __forceinline__ unsigned char* pipe_lds() {
+    __shared__ __attribute__((aligned(1024))) unsigned char buf[TILEB];
+    return buf;
+}
+
 // One query tile (BM rows of head bh) from start to finish; the kernels below run one or two.
 // VL: the rows belong to one sequence of a packed batch described by `sg` (token-major rows,
 // own query and key lengths, causal diagonal offset); otherwise the [B, H, N, d] layout.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false>
+// SPLITM: the masked steps take two-term probabilities (a tile with a row that sees fewer than
+// BN keys).
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false>
 __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, const SeqGeom& sg = SeqGeom{}) {
     constexpr int WR = 32 * RB;             // query rows per wave
     constexpr int BM = 4 * WR;              // query rows per workgroup
@@ -83,13 +101,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     constexpr float kTau = PRECISE ? 8.0f : 0.0f;
     static_assert(LPW >= 1 && LPW * 4 * 1024 == TILEB, "tile must split into 1 KiB pieces");
 
-    // Four separate LDS objects (not offsets into one array): the compiler must wait for an
-    // outstanding global->LDS load before any LDS read it cannot prove disjoint from it, and
-    // distinct objects are what lets it prove that.
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf0[TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char kbuf1[TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf0[TILEB];
-    __shared__ __attribute__((aligned(1024))) unsigned char vbuf1[TILEB];
+    unsigned char* const kbuf0 = pipe_lds<TILEB, 0>();
+    unsigned char* const kbuf1 = pipe_lds<TILEB, 1>();
+    unsigned char* const vbuf0 = pipe_lds<TILEB, 2>();
+    unsigned char* const vbuf1 = pipe_lds<TILEB, 3>();
     constexpr int KB0 = 0, KB1 = 1, VB0 = 2, VB1 = 3;
     auto buf = [&](int id) __attribute__((always_inline)) -> unsigned char* {
         return id == KB0 ? kbuf0 : id == KB1 ? kbuf1 : id == VB0 ? vbuf0 : vbuf1;
@@ -392,9 +407,12 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB)));
         return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
-    auto fast_body = [&](auto par_c, auto masked_c, int j) __attribute__((always_inline)) {
+    auto fast_body = [&](auto par_c, auto masked_c, auto split_c, int j) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_c)::value;
         constexpr bool MASKED = decltype(masked_c)::value;
+        // two-term probabilities for tile j: always with a float32 output; with a bf16 output
+        // when the caller asks (masked tiles of a wave whose rows see fewer than BN keys)
+        constexpr bool SPLIT = PRECISE || decltype(split_c)::value;
         f32x16 (&s_cur)[RB][NKB] = PAR == 0 ? sA : sB;
         f32x16 (&s_nxt)[RB][NKB] = PAR == 0 ? sB : sA;
         constexpr int KB_THIS = PAR == 0 ? KB0 : KB1, KB_OTHER = PAR == 0 ? KB1 : KB0;
@@ -439,7 +457,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                     rs[rb][(e / 2) & 1] += p0 + p1;
                     const int pc = f / 8, w = (f % 8) / 2;
                     ph[rb][pc][w] = pack_bf16x2(p0, p1);
-                    if constexpr (PRECISE)
+                    if constexpr (SPLIT)
                         pl[rb][pc][w] = pack_bf16x2(p0 - bf16_lo_to_f32(ph[rb][pc][w]), p1 - bf16_hi_to_f32(ph[rb][pc][w]));
                 }
             kf = kf1;
@@ -460,7 +478,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
                 acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, ph[rb][pc]), acc[rb][db], 0, 0, 0);
-                if constexpr (PRECISE)
+                if constexpr (SPLIT)
                     acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pl[rb][pc]), acc[rb][db], 0, 0, 0);
             }
             if (i < HB) {
@@ -533,7 +551,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     // MASKED applies the key mask to tile j+1; a tile with no visible key for a row leaves that
     // row's statistics untouched and contributes zero probability.  A wave whose rows see no key
     // of tile j (causal) only helps with the loads and the barrier.
-    auto step = [&](auto par_c, auto masked_c, int j) __attribute__((always_inline)) {
+    auto step = [&](auto par_c, auto masked_c, auto split_c, int j) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_c)::value;
         constexpr int KB_THIS = PAR == 0 ? KB0 : KB1;
         constexpr int VB_OTHER = PAR == 0 ? VB1 : VB0;
@@ -542,7 +560,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
             rescale_pend = false;
         }
         if (j < n_w) {
-            fast_body(par_c, masked_c, j);
+            fast_body(par_c, masked_c, split_c, j);
         } else {
             const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, kbase, j + 2);
             const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, kbase, j + 1);
@@ -559,6 +577,11 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     using P1 = std::integral_constant<int, 1>;
     using Mk = std::true_type;
     using Pl = std::false_type;
+    using NSp = std::false_type;
+    // masked steps of a tile with a row that sees fewer than BN keys take the two-term
+    // probabilities (SPLITM); that row's few probabilities are not averaged
+    using MSp = std::integral_constant<bool, SPLITM>;
+    auto mstep = [&](auto par_c, int jj) __attribute__((always_inline)) { step(par_c, Mk{}, MSp{}, jj); };
 
     // prologue: K_0, K_1, V_0 into their buffers; S_0 and its preparation
     load_tile(std::false_type{}, 0, KB0);
@@ -578,22 +601,22 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     jm = jm < n_tiles ? jm : n_tiles;
     int j = 0;
     for (; j + 2 <= jm; j += 2) {
-        step(P0{}, Pl{}, j);
-        step(P1{}, Pl{}, j + 1);
+        step(P0{}, Pl{}, NSp{}, j);
+        step(P1{}, Pl{}, NSp{}, j + 1);
     }
     if (j < jm) {
-        step(P0{}, Pl{}, j);
+        step(P0{}, Pl{}, NSp{}, j);
         ++j;
     }
     if ((j & 1) && j < n_tiles) {
-        step(P1{}, Mk{}, j);
+        mstep(P1{}, j);
         ++j;
     }
     for (; j + 2 <= n_tiles; j += 2) {
-        step(P0{}, Mk{}, j);
-        step(P1{}, Mk{}, j + 1);
+        mstep(P0{}, j);
+        mstep(P1{}, j + 1);
     }
-    if (j < n_tiles) step(P0{}, Mk{}, j);
+    if (j < n_tiles) mstep(P0{}, j);
 
     // epilogue.  Output register r of block db is O[qrow][32db + 8(r/4) + 4hh + r%4].
 #pragma unroll
@@ -624,45 +647,71 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     }
 }
 
+// Runs query tile qt.  Under the causal mask the tile takes the two-term probabilities in its
+// masked steps only when one of its rows sees fewer than BN keys (Lk keys in all, key j
+// visible to row i iff j <= i + dlt) -- the first tile of a head, in practice -- and the plain
+// instantiation otherwise, so the diagonal tiles of the long rows pay nothing.  Without the
+// causal mask the only masked tile is the ragged end of the keys, and it always takes them.
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL>
+__device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int qt, int Lk, int dlt,
+                                                   const SeqGeom& sg) {
+    constexpr int BM = 128 * RB;
+    if constexpr (OUT_F32 || !CAUSAL) {
+        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true>(a, bh, qt, sg);
+    } else {
+        const bool few = Lk < BN || qt * BM + 1 + dlt < BN;
+        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true>(a, bh, qt, sg);
+        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false>(a, bh, qt, sg);
+    }
+}
+
 // Work item = one query tile, or under the causal mask a pair of tiles (t, n-1-t) with equal
 // total work, so all workgroups of a launch finish together.
 template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32>
 __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     const TilePair tp = pair_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
-    pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32>(a, tp.bh, tp.qt0);
+    int Lk = a.N;
+    if (PAD) {
+        const int s = a.seqlens[tp.bh / a.H];
+        Lk = s < 0 ? 0 : (s > a.N ? a.N : s);
+    }
+    pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false>(a, tp.bh, tp.qt0, Lk, 0, SeqGeom{});
     if (tp.qt1 >= 0) {
         __syncthreads();   // the first tile's LDS buffers are reused
-        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32>(a, tp.bh, tp.qt1);
+        pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
     }
 }
 
 // Packed variable-length sequences ([T, H, d] token-major tensors, per-sequence query and key
 // lengths from prefix sums).  The launch covers the longest query sequence; work item `it` of
-// (sequence, head) takes tile `it` (or, under the causal mask, the pair (it, n-1-it) of the
-// sequence's own n tiles) and items past the sequence's tiles exit at once.
+// (sequence, head) takes tile `it` of the sequence's own n tiles -- or, when the launch pairs
+// causal tiles (enough tiles to fill the chip twice over), the pair (n-1-it, it) -- and items
+// past the sequence's tiles exit at once.  Unpaired causal tiles run from the last (most keys)
+// to the first.
 template <int D, int BN, int RB, bool CAUSAL, bool OUT_F32>
 __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_varlen_kernel(FwdArgs a) {
     constexpr int BM = 128 * RB;
     const int logical = xcd_remap(blockIdx.x, a.total_wgs);
-    const int per = items_per_head(a.n_qtiles, CAUSAL);
+    const bool paired = CAUSAL && a.pair;
+    const int per = paired ? (a.n_qtiles + 1) / 2 : a.n_qtiles;
     const int bh = logical / per;
     const int it = logical - bh * per;
     const int b = bh / a.H;
     const SeqGeom sg = varlen_geom(a, b, bh - b * a.H, D);
     const int n = (sg.Lq + BM - 1) / BM;
     int qt0, qt1 = -1;
-    if (CAUSAL) {
+    if (paired) {
         if (it >= (n + 1) / 2) return;
         qt0 = n - 1 - it;
         if (it < qt0) qt1 = it;
     } else {
         if (it >= n) return;
-        qt0 = it;
+        qt0 = CAUSAL ? n - 1 - it : it;
     }
-    pipe_tile<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt0, sg);
+    pipe_tile_dispatch<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt0, sg.Lk, CAUSAL ? sg.dlt : 0, sg);
     if (qt1 >= 0) {
         __syncthreads();
-        pipe_tile<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt1, sg);
+        pipe_tile_dispatch<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt1, sg.Lk, CAUSAL ? sg.dlt : 0, sg);
     }
 }
 

@@ -92,6 +92,14 @@ def test_decode_kernel(shape, mask, d, out_dtype):
     check(lq, lk, 3, d, mask, out_dtype, seed=200 + d, label=f"decode {shape} d={d} {mask} {out_dtype}")
 
 
+def test_prefill_kernel_paired_launch():
+    """Enough causal tiles (32 sequences x 64 heads x 3 tiles) that the launch pairs tiles
+    (n-1-t, t) of each sequence; ragged lengths from 1 to 300, every row checked."""
+    lq = list(W.draw_lengths(33, 32, 1, 300))
+    lq[0] = 300
+    check(lq, lq, 64, 64, "causal_br", BF16, seed=34, label="prefill paired launch")
+
+
 @pytest.mark.parametrize("name", ["decode_c2kv", "decode_c4kv"])
 def test_decode_workloads_full_size(name):
     w = W.PACKED[name]
