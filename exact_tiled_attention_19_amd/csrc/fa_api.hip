@@ -335,7 +335,9 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
     // several times over; otherwise every tile is its own work item
     const bool pair = causal && bh * n_qtiles >= kPairMinTiles;
     const int64_t items = pair ? (n_qtiles + 1) / 2 : n_qtiles;
-    if (bh * items > 0x7fffffff || bh * plan.n_splits > 0x7fffffff || bh * kDecodeMaxRows > 0x7fffffff)
+    // tile kernel grid: head bh on XCD bh % 8, so the head count is rounded up to a multiple of 8
+    const int64_t tile_wgs = (bh + fa::kNumXcd - 1) / fa::kNumXcd * fa::kNumXcd * items;
+    if (tile_wgs > 0x7fffffff || bh * plan.n_splits > 0x7fffffff || bh * kDecodeMaxRows > 0x7fffffff)
         return FA_ERR_INVALID_ARG;
     // outputs must not overlap each other or any input
     const size_t qb = static_cast<size_t>(total_q) * H * d * 2, kb = static_cast<size_t>(total_k) * H * d * 2;
@@ -406,7 +408,7 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
     a.H = H;
     a.N = 0;
     a.n_qtiles = static_cast<int>(n_qtiles);
-    a.total_wgs = static_cast<int>(bh * items);
+    a.total_wgs = static_cast<int>(tile_wgs);
     a.scale = scale;
     a.scale_log2 = scale_log2;
     a.cu_q = cu_q;
@@ -420,7 +422,7 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
     Kernel kern;
     if (d == 64) kern = of32 ? pick_varlen<64, true>(causal) : pick_varlen<64, false>(causal);
     else kern = of32 ? pick_varlen<128, true>(causal) : pick_varlen<128, false>(causal);
-    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(bh * items)), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(tile_wgs)), dim3(kThreads), 0, st, a);
     if (!launched_ok()) return FA_ERR_HIP;
     return FA_OK;
 }

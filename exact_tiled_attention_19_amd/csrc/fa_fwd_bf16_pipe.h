@@ -688,14 +688,21 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
 // causal tiles (enough tiles to fill the chip twice over), the pair (n-1-it, it) -- and items
 // past the sequence's tiles exit at once.  Unpaired causal tiles run from the last (most keys)
 // to the first.
+//
+// XCD placement: head bh runs on XCD bh % 8 (the dispatcher deals workgroup ids to the XCDs
+// round-robin), its work items contiguous there so its tiles share that XCD's L2.  Heads of
+// one sequence are thereby spread over all XCDs and every XCD receives the same mix of short
+// and long sequences; grouping consecutive heads per XCD, as for equal-length heads, would
+// hand whole sequences, and very unequal amounts of work, to single XCDs.
 template <int D, int BN, int RB, bool CAUSAL, bool OUT_F32>
 __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_varlen_kernel(FwdArgs a) {
     constexpr int BM = 128 * RB;
-    const int logical = xcd_remap(blockIdx.x, a.total_wgs);
     const bool paired = CAUSAL && a.pair;
     const int per = paired ? (a.n_qtiles + 1) / 2 : a.n_qtiles;
-    const int bh = logical / per;
-    const int it = logical - bh * per;
+    const HeadItem hi = head_item_xcd(blockIdx.x, a.B * a.H, per);
+    if (hi.bh < 0) return;
+    const int bh = hi.bh;
+    const int it = hi.it;
     const int b = bh / a.H;
     const SeqGeom sg = varlen_geom(a, b, bh - b * a.H, D);
     const int n = (sg.Lq + BM - 1) / BM;

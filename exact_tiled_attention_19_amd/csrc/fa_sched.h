@@ -70,4 +70,22 @@ FA_HD inline TilePair pair_of(int logical, int n_qtiles, bool causal) {
     return t;
 }
 
+// Packed sequences: workgroup id w -> (head, work item) with head bh on XCD bh % kNumXcd and
+// the `per` items of a head contiguous among that XCD's ids.  The grid holds
+// ceil(n_heads / kNumXcd) * kNumXcd * per ids; ids whose head is >= n_heads get bh = -1.
+struct HeadItem {
+    int bh;
+    int it;
+};
+
+FA_HD inline HeadItem head_item_xcd(int w, int n_heads, int per) {
+    HeadItem r;
+    const int local = w / kNumXcd;
+    const int m = local / per;
+    r.it = local - m * per;
+    r.bh = w % kNumXcd + kNumXcd * m;
+    if (r.bh >= n_heads) r.bh = -1;
+    return r;
+}
+
 }  // namespace fa

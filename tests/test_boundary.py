@@ -266,6 +266,15 @@ def test_sched_mapping_is_bijective(tmp_path):
         "        if (t.qt0 + t.qt1 != nq - 1) ++bad; } }\n"
         "    for (int x : seen) if (x != 1) ++bad;\n"
         "  }\n"
+        "  // packed sequences: head bh on XCD bh % 8, every (head, item) exactly once\n"
+        "  for (int nh : {1, 3, 8, 13, 256, 300}) for (int per : {1, 2, 5, 16}) {\n"
+        "    const int grid = (nh + 7) / 8 * 8 * per;\n"
+        "    std::vector<int> seen(nh * per, 0);\n"
+        "    for (int w = 0; w < grid; ++w) { fa::HeadItem t = fa::head_item_xcd(w, nh, per);\n"
+        "      if (t.bh < 0) continue; if (t.bh >= nh || t.it < 0 || t.it >= per || t.bh % 8 != w % 8) { ++bad; continue; }\n"
+        "      ++seen[t.bh * per + t.it]; }\n"
+        "    for (int x : seen) if (x != 1) ++bad;\n"
+        "  }\n"
         '  std::printf("bad=%d\\n", bad);\n'
         "  return bad != 0;\n"
         "}\n")
