@@ -248,7 +248,7 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
 constexpr int kDecodeMaxRows = 4;
 // Workgroups the decoding kernel aims for (8 per CU), and the fewest keys per range.
 constexpr int64_t kDecodeTargetWgs = 2048;
-constexpr int64_t kDecodeMinKeys = 256;
+constexpr int64_t kDecodeMinKeys = 512;
 // Tile kernel on packed sequences: fewest tiles (over all sequences and heads, counted at the
 // longest query sequence) for which causal tiles are paired.
 constexpr int64_t kPairMinTiles = 4096;

@@ -73,7 +73,7 @@ def test_prefill_kernel(shape, mask, d, out_dtype):
     check(lq, lk, 2, d, mask, out_dtype, seed=100 + d, label=f"prefill {shape} d={d} {mask} {out_dtype}")
 
 
-# decoding-kernel shapes (longest query sequence <= 4 rows): one key range (<= 256 keys) and
+# decoding-kernel shapes (longest query sequence <= 4 rows): one key range (<= 512 keys) and
 # several ranges merged; empty key sets; more query rows than keys
 DECODE = {
     "one_row_split": ([1] * 5, [0, 1, 300, 4097, 64]),
