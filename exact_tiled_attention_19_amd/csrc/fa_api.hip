@@ -30,22 +30,31 @@ using Kernel = void (*)(fa::FwdArgs);
 
 struct Launch {
     Kernel kern;
-    int bm;       // query rows per tile
-    bool paired;  // causal tiles are processed in pairs (one work item = tiles t and n-1-t)
+    int bm;            // query rows per tile
+    bool paired;       // causal tiles are processed in pairs (one work item = tiles t and n-1-t)
+    int threads = kThreads;
 };
 
 // Kernel variants, all computing the same function and passing the same tests:
-//   0  software-pipelined kernel (direct-to-LDS loads, MFMA/VALU overlap)   -- production
+//   0  software-pipelined kernel (direct-to-LDS loads, MFMA/VALU overlap)   -- production; the
+//      eight-wave form of variant 3 for long causal d = 128 heads, else four waves
 //   1  straightforward double-buffered kernel, LDS transpose reads of V
 //   2  the same with V^T gathered by 16-bit LDS reads
-constexpr int kNumVariants = 3;
+//   3  the pipelined kernel with eight waves and 256-row tiles at every size (d = 128 only)
+constexpr int kNumVariants = 4;
+// fa_fwd takes the eight-wave kernel for causal d = 128 launches with at least this many
+// 256-row tiles (over all heads); smaller grids keep two 128-row workgroups per CU.
+constexpr int64_t kWave8MinTiles = 1024;
 
 template <int D, bool CAUSAL, bool PAD, bool OUTF32>
 Launch pick_bf16_variant(int variant) {
     switch (variant) {
         case 0: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32>, 128, true};
         case 1: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>, 128, false};
-        default: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>, 128, false};
+        case 2: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>, 128, false};
+        default:
+            if constexpr (D == 128) return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32, 8>, 256, true, 512};
+            else return {nullptr, 0, false};
     }
 }
 
@@ -83,6 +92,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_DTYPE_F32 && out_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_DTYPE_F32 && variant != 0) return FA_ERR_UNSUPPORTED;
+    if (variant == 3 && d != 128) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
     if ((mask_kind & FA_MASK_KEY_PADDING) && !seqlens) return FA_ERR_INVALID_ARG;
@@ -90,6 +100,10 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (lse && !aligned(lse, 4)) return FA_ERR_INVALID_ARG;
     if ((mask_kind & FA_MASK_KEY_PADDING) && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
     // ---- kernel selection ----
+    // production choice: long causal d = 128 heads take the eight-wave kernel
+    if (variant == 0 && in_dtype == FA_DTYPE_BF16 && d == 128 && (mask_kind & FA_MASK_CAUSAL) &&
+        static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 255) / 256) >= kWave8MinTiles)
+        variant = 3;
     Launch L;
     if (in_dtype == FA_DTYPE_BF16) {
         const bool of32 = out_dtype == FA_DTYPE_F32;
@@ -133,7 +147,8 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     args.scale = scale;
     args.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
 
-    hipLaunchKernelGGL(L.kern, dim3(static_cast<unsigned>(total)), dim3(kThreads), 0,
+    if (!L.kern) return FA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(L.kern, dim3(static_cast<unsigned>(total)), dim3(L.threads), 0,
                        static_cast<hipStream_t>(stream), args);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) {

@@ -9,7 +9,8 @@
 // work is arranged on the chip:
 //
 //   * One workgroup of four wave64s per (batch, head, 128-row query tile), 32 rows per wave,
-//     two workgroups per CU.  Under the causal mask a workgroup runs the tile pair (t, n-1-t).
+//     two workgroups per CU (or eight waves and 256 rows, one workgroup per CU, for long
+//     causal d = 128 heads).  Under the causal mask a workgroup runs the tile pair (t, n-1-t).
 //   * Pipeline.  Iteration j has two phases.  Phase A issues the MFMAs of
 //     S_{j+1}^T = K_{j+1} Q^T while the vector ALUs exponentiate the already shifted scores of
 //     tile j, sum them and pack P_j to bf16.  Phase B issues O^T += V_j^T P_j^T while the vector
@@ -80,11 +81,11 @@ __device__ __forceinline__ unsigned char* pipe_lds() {
 // VL: the rows belong to one sequence of a packed batch described by `sg` (token-major rows,
 // own query and key lengths, causal diagonal offset); otherwise the [B, H, N, d] layout.
 // SPLITM: the masked steps take two-term probabilities (a tile with a row that sees fewer than
-// BN keys).
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false>
+// BN keys).  NW: waves per workgroup (4, or 8 for one 256-row workgroup per CU).
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false, int NW = 4>
 __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, const SeqGeom& sg = SeqGeom{}) {
     constexpr int WR = 32 * RB;             // query rows per wave
-    constexpr int BM = 4 * WR;              // query rows per workgroup
+    constexpr int BM = NW * WR;             // query rows per workgroup
     constexpr int KC = D / 16;              // k-steps of the S MFMA
     constexpr int NKB = BN / 32;            // 32-key blocks per tile
     constexpr int NDB = D / 32;             // 32-wide output blocks
@@ -92,14 +93,14 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     constexpr int ROWB = D * 2;             // bytes per K/V row in LDS (no padding)
     constexpr int TILEB = BN * ROWB;        // bytes per K or V tile
     constexpr int CPR = D / 8;              // 16-byte chunks per row
-    constexpr int LPW = TILEB / 1024 / 4;   // direct-to-LDS instructions per wave per tile
+    constexpr int LPW = TILEB / 1024 / NW;  // direct-to-LDS instructions per wave per tile
     constexpr bool PRECISE = OUT_F32;
     // Shift threshold (log2 units).  With a bf16 output the probabilities enter the PV product
     // as single bf16 values, so the shift tracks the exact row maximum (threshold 0: the largest
     // probability is then exactly 1 and carries no rounding); with the two-term split used for
     // a float32 output a shift lagging by up to 8 costs nothing.
     constexpr float kTau = PRECISE ? 8.0f : 0.0f;
-    static_assert(LPW >= 1 && LPW * 4 * 1024 == TILEB, "tile must split into 1 KiB pieces");
+    static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "tile must split into 1 KiB pieces");
 
     unsigned char* const kbuf0 = pipe_lds<TILEB, 0>();
     unsigned char* const kbuf1 = pipe_lds<TILEB, 1>();
@@ -219,7 +220,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     uint32_t koff[LPW], voff[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-        const int p = (i * 4 + wave) * 64 + lane;
+        const int p = (i * NW + wave) * 64 + lane;
         const int row = p / CPR;
         const int pch = p % CPR;
         koff[i] = row * RSB + (pch ^ swz_k<D>(row)) * 16;
@@ -230,7 +231,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         const uint32_t t0 = (uint32_t)tile * (uint32_t)(BN * RSB);
 #pragma unroll
         for (int i = 0; i < LPW; ++i)
-            buffer_load_lds16(IS_V ? vrs : krs, buf(buf_off) + (i * 4 + wave) * 1024,
+            buffer_load_lds16(IS_V ? vrs : krs, buf(buf_off) + (i * NW + wave) * 1024,
                               (IS_V ? voff[i] : koff[i]) + t0);
     };
 
@@ -437,8 +438,8 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         bf16x8 kf1 = kfrag(KB_OTHER, 1);
 #pragma unroll
         for (int i = 0; i < NSF; ++i) {
-            if (i < LPW) buffer_load_lds16(krs_t, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i]);
-            else if (i < 2 * LPW) buffer_load_lds16(vrs_t, buf(VB_OTHER) + ((i - LPW) * 4 + wave) * 1024, voff[i - LPW]);
+            if (i < LPW) buffer_load_lds16(krs_t, buf(KB_THIS) + (i * NW + wave) * 1024, koff[i]);
+            else if (i < 2 * LPW) buffer_load_lds16(vrs_t, buf(VB_OTHER) + ((i - LPW) * NW + wave) * 1024, voff[i - LPW]);
             bf16x8 kf2 = kf1;           // operands are read two fragments ahead
             if (i + 2 < NSF) kf2 = kfrag(KB_OTHER, i + 2);
             const int c = i / NKB, kb = i % NKB;
@@ -566,8 +567,8 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
             const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, kbase, j + 1);
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                buffer_load_lds16(krs_t, buf(KB_THIS) + (i * 4 + wave) * 1024, koff[i]);
-                buffer_load_lds16(vrs_t, buf(VB_OTHER) + (i * 4 + wave) * 1024, voff[i]);
+                buffer_load_lds16(krs_t, buf(KB_THIS) + (i * NW + wave) * 1024, koff[i]);
+                buffer_load_lds16(vrs_t, buf(VB_OTHER) + (i * NW + wave) * 1024, voff[i]);
             }
         }
         wait_loads();
@@ -652,33 +653,37 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 // visible to row i iff j <= i + dlt) -- the first tile of a head, in practice -- and the plain
 // instantiation otherwise, so the diagonal tiles of the long rows pay nothing.  Without the
 // causal mask the only masked tile is the ragged end of the keys, and it always takes them.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL>
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL, int NW = 4>
 __device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int qt, int Lk, int dlt,
                                                    const SeqGeom& sg) {
-    constexpr int BM = 128 * RB;
+    constexpr int BM = NW * 32 * RB;
     if constexpr (OUT_F32 || !CAUSAL) {
-        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true>(a, bh, qt, sg);
+        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW>(a, bh, qt, sg);
     } else {
         const bool few = Lk < BN || qt * BM + 1 + dlt < BN;
-        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true>(a, bh, qt, sg);
-        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false>(a, bh, qt, sg);
+        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW>(a, bh, qt, sg);
+        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW>(a, bh, qt, sg);
     }
 }
 
 // Work item = one query tile, or under the causal mask a pair of tiles (t, n-1-t) with equal
-// total work, so all workgroups of a launch finish together.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32>
-__global__ void __launch_bounds__(256, 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
+// total work, so all workgroups of a launch finish together.  NW = 4: 128-row tiles, two
+// workgroups per CU.  NW = 8: 256-row tiles, one workgroup per CU (still two waves per SIMD),
+// which stages each K/V tile into LDS once for 256 rows instead of twice for 128; it pays off
+// for long causal d = 128 heads (+2-3 % at N = 8192 and 131072) and loses where the grid is
+// small or the sequences short, so the host picks it only there.
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 4>
+__global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     const TilePair tp = pair_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
     int Lk = a.N;
     if (PAD) {
         const int s = a.seqlens[tp.bh / a.H];
         Lk = s < 0 ? 0 : (s > a.N ? a.N : s);
     }
-    pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false>(a, tp.bh, tp.qt0, Lk, 0, SeqGeom{});
+    pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW>(a, tp.bh, tp.qt0, Lk, 0, SeqGeom{});
     if (tp.qt1 >= 0) {
         __syncthreads();   // the first tile's LDS buffers are reused
-        pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
+        pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
     }
 }
 

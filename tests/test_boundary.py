@@ -105,6 +105,7 @@ UNSUPPORTED = {
     "unknown variant": dict(variant=99),
     "negative variant": dict(variant=-1),
     "f32 with variant 1": dict(ind=F32, outd=F32, variant=1),
+    "eight-wave variant at d 64": dict(variant=3),
 }
 
 

@@ -53,10 +53,12 @@ def test_sweep_bf16(N, d, mask):
                                   out_dtype=out_dtype, label=label))
 
 
-@pytest.mark.parametrize("variant", range(1, 3))
+@pytest.mark.parametrize("variant", range(1, 4))
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_variants_bf16(variant, d, mask):
+    if variant == 3 and d == 64:
+        pytest.skip("the eight-wave variant exists for d = 128 only (d = 64 returns FA_ERR_UNSUPPORTED)")
     causal, pad = MASKS[mask]
     B, H, N = 1, 3, 333
     q, k, v, _ = W.random_qkv(B, H, N, d, BF16, seed=77 + d)
