@@ -289,6 +289,11 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     }
     bool rescale_pend = false;
 
+    // Multiplier of the masked steps' fma: scale*log2(e), or the smallest normal float when the
+    // scale is 0 (then every visible t is within 1e-30 of 0, as it should be, and -inf * c
+    // stays -inf instead of NaN).
+    const float c_mask = a.scale_log2 > 0.f ? a.scale_log2 : 1.17549435e-38f;
+
     // Phase B vector work for tile `tile`: mask (edge tiles only), row maximum, lazy shift
     // update, then the shifted scores t = s * scale * log2(e) - m in place.
     auto prep = [&](f32x16 (&s)[RB][NKB], int tile, bool masked) __attribute__((always_inline)) {
@@ -521,7 +526,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                     m_run[rb] = m_new;
                     l_run[rb] *= alpha;
                     alpha_pend[rb] = alpha;
-                    mx[rb][0] = -m_new;      // reuse: the shift for the fma slots
+                    // reuse: the shift for the fma slots.  In masked tiles it is kept finite (a
+                    // row with no visible key yet has m = -inf), so that with the positive
+                    // multiplier c_mask a hidden score -inf stays -inf through the fma.
+                    mx[rb][0] = (MASKED && m_new == kNegInf) ? 0.f : -m_new;
                 }
             } else {
                 constexpr int E = (NE + NFMA - 1) / NFMA;
@@ -532,8 +540,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                     for (int e = 0; e < E; ++e) {
                         const int f = k0 + e;
                         if (f < NE) {
-                            float t = fmaf(s_nxt[rb][f / 16][f % 16], a.scale_log2, mx[rb][0]);
-                            if constexpr (MASKED) t = (s_nxt[rb][f / 16][f % 16] == kNegInf) ? kNegInf : t;
+                            const float t = fmaf(s_nxt[rb][f / 16][f % 16], MASKED ? c_mask : a.scale_log2, mx[rb][0]);
                             s_nxt[rb][f / 16][f % 16] = t;
                         }
                     }
