@@ -24,8 +24,10 @@ from .binding import (  # noqa: F401
     backward,
     fa_bwd,
     fa_fwd,
+    fa_fwd_dropout,
     fa_fwd_varlen,
     forward,
+    forward_dropout,
     forward_varlen,
     load_library,
     status_str,

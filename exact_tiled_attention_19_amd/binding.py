@@ -41,6 +41,8 @@ _I = ctypes.c_int
 SIGNATURES = {
     "fa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP]),
     "fa_fwd_variant": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP, _I]),
+    "fa_fwd_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, ctypes.c_float,
+                            ctypes.c_uint64, ctypes.c_uint32, _I, _I, _VP]),
     "fa_bwd": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I,
                     _VP]),
     "fa_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I,
@@ -169,6 +171,53 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
                 _ptr(seqlens), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype], stream, variant)
     _check(st)
     return out, lse
+
+
+def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, p_drop, seed, offset, in_dtype, out_dtype,
+                   stream) -> int:
+    """Raw call of the forward with dropout through the C ABI (pointers as ints or None)."""
+    return load_library().fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), mask_kind, seqlens,
+                                         ctypes.c_float(p_drop), ctypes.c_uint64(seed), ctypes.c_uint32(offset),
+                                         in_dtype, out_dtype, stream)
+
+
+def forward_dropout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, p: float, seed: int, offset: int = 0, *,
+                    scale: Optional[float] = None, causal: bool = False, seqlens: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                    lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward with dropout on the probabilities (contract in include/fa.h): returns
+    (O, LSE), LSE before dropout.  q, k, v: [B, H, N, d] contiguous bfloat16 device tensors;
+    p: drop probability (quantised to 1/256); seed (64-bit) and offset (32-bit) select the mask."""
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if q.dtype != torch.bfloat16 or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must be bfloat16")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape or not all(t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must all be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
+    if seqlens is not None:
+        if not seqlens.is_cuda or seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 device tensor with B entries")
+        mask |= FA_MASK_KEY_PADDING
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if lse_out is None:
+        lse_out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse_out.shape != (B, H, N) or lse_out.dtype != torch.float32 or not lse_out.is_contiguous():
+        raise ValueError("lse_out must be a contiguous float32 [B, H, N] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse_out), B, H, N, d, float(scale), mask,
+                        _ptr(seqlens), float(p), int(seed) & 0xFFFFFFFFFFFFFFFF, int(offset) & 0xFFFFFFFF,
+                        FA_DTYPE_BF16, _DTYPE_CODE[out_dtype], stream)
+    _check(st)
+    return out, lse_out
 
 
 def fa_bwd(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask_kind, seqlens, in_dtype,

@@ -78,9 +78,33 @@ Launch pick_f32_mask(int mask) {
     }
 }
 
+// Dropout request of fa_fwd_dropout: drop probability, Philox seed and counter offset.
+struct DropSpec {
+    float p;
+    uint64_t seed;
+    uint32_t offset;
+};
+
+// Byte threshold round(256 p) of the dropout contract, or -1 when p is outside [0, 255.5/256).
+int drop_threshold(float p) {
+    if (!std::isfinite(p) || p < 0.f) return -1;
+    const double t = std::floor(256.0 * static_cast<double>(p) + 0.5);
+    return t <= 255.0 ? static_cast<int>(t) : -1;
+}
+
+template <int D, bool OUTF32>
+Launch pick_bf16_drop(int mask) {
+    switch (mask) {
+        case 0: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, false, false, OUTF32, 4, true>, 128, true};
+        case 1: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, true, false, OUTF32, 4, true>, 128, true};
+        case 2: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, false, true, OUTF32, 4, true>, 128, true};
+        default: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, true, true, OUTF32, 4, true>, 128, true};
+    }
+}
+
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype, int out_dtype,
-           void* stream, int variant) {
+           void* stream, int variant, const DropSpec* drop = nullptr) {
     // ---- validation (host only, before any HIP call) ----
     if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
     if (mask_kind < 0 || mask_kind > (FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
@@ -93,6 +117,8 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (in_dtype == FA_DTYPE_F32 && out_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_DTYPE_F32 && variant != 0) return FA_ERR_UNSUPPORTED;
     if (variant == 3 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (drop && drop_threshold(drop->p) < 0) return FA_ERR_INVALID_ARG;
+    if (drop && in_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
     if (B == 0 || H == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
     if ((mask_kind & FA_MASK_KEY_PADDING) && !seqlens) return FA_ERR_INVALID_ARG;
@@ -101,11 +127,15 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if ((mask_kind & FA_MASK_KEY_PADDING) && !aligned(seqlens, 4)) return FA_ERR_INVALID_ARG;
     // ---- kernel selection ----
     // production choice: long causal d = 128 heads take the eight-wave kernel
-    if (variant == 0 && in_dtype == FA_DTYPE_BF16 && d == 128 && (mask_kind & FA_MASK_CAUSAL) &&
+    if (!drop && variant == 0 && in_dtype == FA_DTYPE_BF16 && d == 128 && (mask_kind & FA_MASK_CAUSAL) &&
         static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 255) / 256) >= kWave8MinTiles)
         variant = 3;
     Launch L;
-    if (in_dtype == FA_DTYPE_BF16) {
+    if (drop) {
+        const bool of32 = out_dtype == FA_DTYPE_F32;
+        if (d == 64) L = of32 ? pick_bf16_drop<64, true>(mask_kind) : pick_bf16_drop<64, false>(mask_kind);
+        else L = of32 ? pick_bf16_drop<128, true>(mask_kind) : pick_bf16_drop<128, false>(mask_kind);
+    } else if (in_dtype == FA_DTYPE_BF16) {
         const bool of32 = out_dtype == FA_DTYPE_F32;
         if (d == 64) L = of32 ? pick_bf16_mask<64, true>(mask_kind, variant) : pick_bf16_mask<64, false>(mask_kind, variant);
         else L = of32 ? pick_bf16_mask<128, true>(mask_kind, variant) : pick_bf16_mask<128, false>(mask_kind, variant);
@@ -132,13 +162,21 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
                 overlaps(lse, static_cast<size_t>(B) * H * N * 4, v, in_bytes)))
         return FA_ERR_INVALID_ARG;
 
-    fa::FwdArgs args;
+    fa::FwdArgs args{};
     args.q = q;
     args.k = k;
     args.v = v;
     args.o = o;
     args.lse = lse;
     args.seqlens = (mask_kind & FA_MASK_KEY_PADDING) ? seqlens : nullptr;
+    if (drop) {
+        const int t = drop_threshold(drop->p);
+        args.drop_k0 = static_cast<uint32_t>(drop->seed);
+        args.drop_k1 = static_cast<uint32_t>(drop->seed >> 32);
+        args.drop_offset = drop->offset;
+        args.drop_t = static_cast<uint32_t>(t);
+        args.drop_keep_scale = static_cast<float>(256.0 / (256 - t));
+    }
     args.B = B;
     args.H = H;
     args.N = N;
@@ -470,6 +508,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype, int out_dtype,
            void* stream) {
     return launch(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, in_dtype, out_dtype, stream, 0);
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+                   float scale, int mask_kind, const int32_t* seqlens, float p_drop, uint64_t seed, uint32_t offset,
+                   int in_dtype, int out_dtype, void* stream) {
+    const DropSpec drop{p_drop, seed, offset};
+    return launch(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, in_dtype, out_dtype, stream, 0, &drop);
 }
 
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

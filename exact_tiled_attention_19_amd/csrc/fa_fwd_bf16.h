@@ -60,6 +60,11 @@ struct FwdArgs {
     int max_q, max_k;      // longest query / key sequence the launch was sized for
     int bottom_right;      // causal alignment: 1 bottom-right, 0 top-left
     int pair;              // causal: a work item is a tile pair (t, n-1-t) of one sequence
+    // dropout on the probabilities (kernels instantiated with dropout only)
+    uint32_t drop_k0, drop_k1;   // Philox key: the seed's low and high words
+    uint32_t drop_offset;        // fourth Philox counter word
+    uint32_t drop_t;             // byte threshold round(256 p): kept iff byte >= drop_t
+    float drop_keep_scale;       // 256 / (256 - drop_t)
 };
 
 // Where the rows of one head of one sequence live, and which keys its queries may see.

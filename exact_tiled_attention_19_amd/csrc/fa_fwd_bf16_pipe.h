@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "fa_fwd_bf16.h"
+#include "fa_dropout.h"
 
 namespace fa {
 
@@ -81,8 +82,11 @@ __device__ __forceinline__ unsigned char* pipe_lds() {
 // VL: the rows belong to one sequence of a packed batch described by `sg` (token-major rows,
 // own query and key lengths, causal diagonal offset); otherwise the [B, H, N, d] layout.
 // SPLITM: the masked steps take two-term probabilities (a tile with a row that sees fewer than
-// BN keys).  NW: waves per workgroup (4, or 8 for one 256-row workgroup per CU).
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false, int NW = 4>
+// BN keys).  NW: waves per workgroup (4, or 8 for one 256-row workgroup per CU).  DROP:
+// dropout on the probabilities that enter the value product (the row sums, and so O's
+// normaliser and the log-sum-exp, take them undropped; kept ones are scaled in the epilogue).
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false, int NW = 4,
+          bool DROP = false>
 __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, const SeqGeom& sg = SeqGeom{}) {
     constexpr int WR = 32 * RB;             // query rows per wave
     constexpr int BM = NW * WR;             // query rows per workgroup
@@ -101,6 +105,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     // a float32 output a shift lagging by up to 8 costs nothing.
     constexpr float kTau = PRECISE ? 8.0f : 0.0f;
     static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "tile must split into 1 KiB pieces");
+    static_assert(!DROP || (RB == 1 && BN == 64 && !VL), "dropout words are laid out for one 32-row block");
 
     unsigned char* const kbuf0 = pipe_lds<TILEB, 0>();
     unsigned char* const kbuf1 = pipe_lds<TILEB, 1>();
@@ -438,6 +443,8 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         float rs[RB][2];
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) rs[rb][0] = rs[rb][1] = 0.f;
+        // dropout words of the current 32-key half of tile j (see dropout_words_fwd)
+        uint32_t dw[4];
         // phase A
         bf16x8 kf = kfrag(KB_OTHER, 0);
         bf16x8 kf1 = kfrag(KB_OTHER, 1);
@@ -451,6 +458,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 s_nxt[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][c], c == 0 ? f32x16{} : s_nxt[rb][kb], 0, 0, 0);
+            if constexpr (DROP) {
+                if ((i * EA) % 16 == 0)   // first slot of a 32-key half
+                    dropout_words_fwd(dw, j * BN, (i * EA) / 16, qrow[0], hh, tc.bh, a.drop_offset, a.drop_k0, a.drop_k1);
+            }
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
@@ -461,10 +472,15 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                     s_cur[rb][fk][fr] = p0;
                     s_cur[rb][fk][fr + 1] = p1;
                     rs[rb][(e / 2) & 1] += p0 + p1;
+                    float d0 = p0, d1 = p1;      // the probabilities entering the value product
+                    if constexpr (DROP) {
+                        d0 = drop_keep(dw[fr / 4], fr % 4, a.drop_t) ? p0 : 0.f;
+                        d1 = drop_keep(dw[fr / 4], fr % 4 + 1, a.drop_t) ? p1 : 0.f;
+                    }
                     const int pc = f / 8, w = (f % 8) / 2;
-                    ph[rb][pc][w] = pack_bf16x2(p0, p1);
+                    ph[rb][pc][w] = pack_bf16x2(d0, d1);
                     if constexpr (SPLIT)
-                        pl[rb][pc][w] = pack_bf16x2(p0 - bf16_lo_to_f32(ph[rb][pc][w]), p1 - bf16_hi_to_f32(ph[rb][pc][w]));
+                        pl[rb][pc][w] = pack_bf16x2(d0 - bf16_lo_to_f32(ph[rb][pc][w]), d1 - bf16_hi_to_f32(ph[rb][pc][w]));
                 }
             kf = kf1;
             kf1 = kf2;
@@ -633,7 +649,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         // packed sequences under the causal mask: a row may see no key at all (bottom-right
         // alignment with more queries than keys); it gets O = 0 and LSE = -inf
         const bool none = VL && CAUSAL && !(l_tot > 0.f);
-        const float inv_l = none ? 0.f : 1.0f / l_tot;
+        const float inv_l = none ? 0.f : (DROP ? a.drop_keep_scale : 1.0f) / l_tot;
         if (qrow[rb] >= N) continue;
         if (hh == 0 && a.lse) a.lse[lbase + qrow[rb]] = none ? kNegInf : (m_run[rb] + __log2f(l_tot)) * kLn2;
 #pragma unroll
@@ -660,16 +676,16 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 // visible to row i iff j <= i + dlt) -- the first tile of a head, in practice -- and the plain
 // instantiation otherwise, so the diagonal tiles of the long rows pay nothing.  Without the
 // causal mask the only masked tile is the ragged end of the keys, and it always takes them.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL, int NW = 4>
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL, int NW = 4, bool DROP = false>
 __device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int qt, int Lk, int dlt,
                                                    const SeqGeom& sg) {
     constexpr int BM = NW * 32 * RB;
     if constexpr (OUT_F32 || !CAUSAL) {
-        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW>(a, bh, qt, sg);
+        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP>(a, bh, qt, sg);
     } else {
         const bool few = Lk < BN || qt * BM + 1 + dlt < BN;
-        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW>(a, bh, qt, sg);
-        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW>(a, bh, qt, sg);
+        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP>(a, bh, qt, sg);
+        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW, DROP>(a, bh, qt, sg);
     }
 }
 
@@ -679,7 +695,7 @@ __device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int
 // which stages each K/V tile into LDS once for 256 rows instead of twice for 128; it pays off
 // for long causal d = 128 heads (+2-3 % at N = 8192 and 131072) and loses where the grid is
 // small or the sequences short, so the host picks it only there.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 4>
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 4, bool DROP = false>
 __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     const TilePair tp = pair_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
     int Lk = a.N;
@@ -687,10 +703,10 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) fa_fwd_bf16_pipe_ker
         const int s = a.seqlens[tp.bh / a.H];
         Lk = s < 0 ? 0 : (s > a.N ? a.N : s);
     }
-    pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW>(a, tp.bh, tp.qt0, Lk, 0, SeqGeom{});
+    pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW, DROP>(a, tp.bh, tp.qt0, Lk, 0, SeqGeom{});
     if (tp.qt1 >= 0) {
         __syncthreads();   // the first tile's LDS buffers are reused
-        pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
+        pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW, DROP>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
     }
 }
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 10200 /* major*10000 + minor*100 + patch */
+#define FA_VERSION 10300 /* major*10000 + minor*100 + patch */
 
 typedef enum {
     FA_OK = 0,
@@ -84,6 +84,32 @@ enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 };
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
            int in_dtype, int out_dtype, void* stream);
+
+/*
+ * fa_fwd_dropout -- fa_fwd with dropout on the attention probabilities:
+ *
+ *     O = (P * Z) V,   Z_ij = keep_ij * 256 / (256 - t),   t = round(256 * p_drop),
+ *
+ * with P the probabilities of fa_fwd; the LSE output is that of P, before dropout.  The
+ * cswork.org page asks that dropout be tested against the implementation's random-number and
+ * reproducibility contract (section "Does subtracting the maximum solve every numerical
+ * issue?"); this is the contract:
+ *   keep_ij for query row i and key j of head bh = b * H + h is
+ *       byte (4 * (i % 4) + (j % 4)) of Philox4x32-10(counter = (j / 4, i / 4, bh, offset),
+ *                                                     key = (seed & 0xffffffff, seed >> 32)) >= t,
+ *   the 16 output bytes taken from the four 32-bit words in order, each little-endian
+ *   (Philox4x32-10: Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+ *   3", SC '11).  The same (seed, offset) gives the same mask on every run and every device;
+ *   the drop probability is quantised to 1/256.
+ *
+ *   p_drop    drop probability, finite, 0 <= p_drop < 255.5/256 (else FA_ERR_INVALID_ARG).
+ *   seed, offset   Philox key and fourth counter word.
+ *   Other arguments as for fa_fwd; in_dtype must be BF16 (F32 inputs: FA_ERR_UNSUPPORTED).
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
+                   float p_drop, uint64_t seed, uint32_t offset,
+                   int in_dtype, int out_dtype, void* stream);
 
 /*
  * fa_fwd_variant -- fa_fwd with an explicit kernel variant, for tests and tuning only.

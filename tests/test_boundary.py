@@ -228,6 +228,29 @@ def test_varlen_workspace_size():
         assert ws(B, H, mq, mk, d) == n                 # deterministic
 
 
+def drop_call(p=0.1, seed=1, offset=0, ind=BF16, outd=BF16, d=64, N=16, **kw):
+    a = dict(q=P, k=P2, v=P3, o=P4, lse=None, B=1, H=1, scale=0.125, mask=0, seqlens=None)
+    a.update(kw)
+    return fa.fa_fwd_dropout(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], N, d, a["scale"], a["mask"],
+                             a["seqlens"], p, seed, offset, ind, outd, None)
+
+
+DROP_INVALID = {"p negative": dict(p=-0.01), "p one": dict(p=1.0), "p nan": dict(p=float("nan")),
+                "p inf": dict(p=float("inf")), "null q": dict(q=None), "o aliases q": dict(o=P),
+                "misaligned v": dict(v=P3 + 2), "mask bit 4": dict(mask=4)}
+
+
+@pytest.mark.parametrize("name", sorted(DROP_INVALID))
+def test_dropout_invalid_argument_rejected_on_host(name):
+    assert drop_call(**DROP_INVALID[name]) == fa.FA_ERR_INVALID_ARG, name
+
+
+def test_dropout_unsupported_and_empty():
+    assert drop_call(ind=F32, outd=F32) == fa.FA_ERR_UNSUPPORTED
+    assert drop_call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert drop_call(N=0, q=None, k=None, v=None, o=None) == fa.FA_OK
+
+
 def test_python_forward_rejects_host_tensors():
     import torch
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
