@@ -273,6 +273,9 @@ def main() -> int:
                     help="override the workload's Q/K gain (c3 uses 3: logit std ~ 9; 1 gives flat rows)")
     ap.add_argument("--cpu-rows", type=int, default=6144, help="oracle rows per head for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout", type=float, default=None,
+                    help="time the forward with dropout of this probability on the attention weights "
+                         "(fa_fwd_dropout, Philox seed 1234)")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd: dQ, dK, dV) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -319,6 +322,11 @@ def main() -> int:
     def step():
         fa.forward(q, k, v, scale=x.scale, causal=causal, seqlens=seq, out_dtype=out_dtype,
                    out=o, lse_out=lse, variant=args.variant)
+
+    if args.dropout is not None:
+        def step():
+            fa.forward_dropout(q, k, v, args.dropout, 1234, 0, scale=x.scale, causal=causal, seqlens=seq,
+                               out_dtype=out_dtype, out=o, lse_out=lse)
 
     if args.bwd:
         # the forward's bf16 output and LSE, and a seeded upstream gradient of the same shape
@@ -375,7 +383,8 @@ def main() -> int:
     traffic = recorded_traffic(workload_id)
 
     res = {
-        "metric": METRIC if not args.bwd else "attention bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's FLOP), 1 GPU",
+        "metric": (METRIC if not args.bwd else "attention bwd TFLOP/s (dQ, dK, dV; 2.5x the forward's FLOP), 1 GPU")
+        + (f", dropout p={args.dropout}" if args.dropout is not None else ""),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -395,6 +404,7 @@ def main() -> int:
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name,
             "flop_per_step": flops, "compulsory_bytes_per_step": nbytes, "variant": args.variant,
             "pass": "backward" if args.bwd else "forward",
+            "dropout": args.dropout,
         },
         "roofline": {
             "bound": bound,
@@ -410,7 +420,7 @@ def main() -> int:
         res["roofline"]["note"] = ("three kernels per step (row term, dK/dV, dQ); achieved counts the pass's "
                                    "2.5x-forward FLOP over their combined time, which executes 3.5x")
         res["roofline"]["traffic"] = None
-    if not args.no_cpu_baseline and not args.bwd:
+    if not args.no_cpu_baseline and not args.bwd and args.dropout is None:
         print(f"[bench] timing the fp64 oracle on {args.cpu_rows} rows per head", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_rows, w.N))
     print(json.dumps(res), flush=True)

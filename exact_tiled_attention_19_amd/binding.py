@@ -48,6 +48,8 @@ SIGNATURES = {
     "fa_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I,
                            _VP, ctypes.c_size_t, _I, _I, _VP]),
     "fa_fwd_varlen_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "fa_bwd_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP,
+                            ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32, _I, _I, _VP]),
     "fa_variant_count": (_I, []),
     "fa_status_str": (ctypes.c_char_p, [_I]),
     "fa_last_hip_error": (_I, []),
@@ -230,14 +232,16 @@ def fa_bwd(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask_kin
 def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
              dout: torch.Tensor, *, scale: Optional[float] = None, causal: bool = False,
              seqlens: Optional[torch.Tensor] = None, out: Optional[Tuple[torch.Tensor, ...]] = None,
-             delta: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+             delta: Optional[torch.Tensor] = None,
+             dropout: Optional[Tuple[float, int, int]] = None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """Gradients (dQ, dK, dV) of the forward pass on the GPU, float32.
 
     q, k, v: the forward inputs; o, lse: what ``forward`` returned for them (o in bfloat16);
     dout: the gradient arriving at o.  All [B, H, N, d] contiguous bfloat16 device tensors (lse
     float32 [B, H, N]).  scale, causal and seqlens as for ``forward``.
     out: optional preallocated (dq, dk, dv) float32 tensors; delta: optional float32 [B, H, N]
-    workspace (allocated here when omitted).
+    workspace (allocated here when omitted).  dropout: (p, seed, offset) of the
+    ``forward_dropout`` call that produced o and lse, whose mask is regenerated.
     """
     ts = (q, k, v, o, dout)
     if not all(t.is_cuda for t in ts) or not lse.is_cuda:
@@ -267,6 +271,16 @@ def backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
     elif delta.shape != (B, H, N) or delta.dtype != torch.float32 or not delta.is_contiguous():
         raise ValueError("delta must be a contiguous float32 [B, H, N] tensor")
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    if dropout is not None:
+        p, seed, offset = dropout
+        st = load_library().fa_bwd_dropout(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(delta),
+                                           _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), B, H, N, d, ctypes.c_float(scale),
+                                           mask, _ptr(seqlens), ctypes.c_float(p),
+                                           ctypes.c_uint64(int(seed) & 0xFFFFFFFFFFFFFFFF),
+                                           ctypes.c_uint32(int(offset) & 0xFFFFFFFF), FA_DTYPE_BF16, FA_DTYPE_F32,
+                                           stream)
+        _check(st)
+        return out
     st = fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(delta), _ptr(out[0]), _ptr(out[1]),
                 _ptr(out[2]), B, H, N, d, float(scale), mask, _ptr(seqlens), FA_DTYPE_BF16, FA_DTYPE_F32, stream)
     _check(st)

@@ -198,13 +198,13 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 using BwdKernel = void (*)(fa::BwdArgs);
 
-template <int D>
+template <int D, bool DROP>
 void pick_bwd(int mask_kind, BwdKernel& dkdv, BwdKernel& dq) {
     switch (mask_kind) {
-        case 0: dkdv = fa::fa_bwd_dkdv_kernel<D, false, false>; dq = fa::fa_bwd_dq_kernel<D, false, false>; break;
-        case 1: dkdv = fa::fa_bwd_dkdv_kernel<D, true, false>; dq = fa::fa_bwd_dq_kernel<D, true, false>; break;
-        case 2: dkdv = fa::fa_bwd_dkdv_kernel<D, false, true>; dq = fa::fa_bwd_dq_kernel<D, false, true>; break;
-        default: dkdv = fa::fa_bwd_dkdv_kernel<D, true, true>; dq = fa::fa_bwd_dq_kernel<D, true, true>; break;
+        case 0: dkdv = fa::fa_bwd_dkdv_kernel<D, false, false, DROP>; dq = fa::fa_bwd_dq_kernel<D, false, false, DROP>; break;
+        case 1: dkdv = fa::fa_bwd_dkdv_kernel<D, true, false, DROP>; dq = fa::fa_bwd_dq_kernel<D, true, false, DROP>; break;
+        case 2: dkdv = fa::fa_bwd_dkdv_kernel<D, false, true, DROP>; dq = fa::fa_bwd_dq_kernel<D, false, true, DROP>; break;
+        default: dkdv = fa::fa_bwd_dkdv_kernel<D, true, true, DROP>; dq = fa::fa_bwd_dq_kernel<D, true, true, DROP>; break;
     }
 }
 
@@ -219,7 +219,8 @@ bool launched_ok() {
 
 int bwd_launch(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale,
-               int mask_kind, const int32_t* seqlens, int in_dtype, int grad_dtype, void* stream) {
+               int mask_kind, const int32_t* seqlens, int in_dtype, int grad_dtype, void* stream,
+               const DropSpec* drop = nullptr) {
     // ---- validation (host only, before any HIP call) ----
     if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
     if (mask_kind < 0 || mask_kind > (FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
@@ -229,6 +230,7 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     if (d <= 0) return FA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (in_dtype != FA_DTYPE_BF16 || grad_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+    if (drop && drop_threshold(drop->p) < 0) return FA_ERR_INVALID_ARG;
     if (B == 0 || H == 0 || N == 0) return FA_OK;
     if (!q || !k || !v || !o || !lse || !dout || !delta || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
     if ((mask_kind & FA_MASK_KEY_PADDING) && !seqlens) return FA_ERR_INVALID_ARG;
@@ -255,7 +257,7 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
             if (overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_INVALID_ARG;
     }
 
-    fa::BwdArgs args;
+    fa::BwdArgs args{};
     args.q = q;
     args.k = k;
     args.v = v;
@@ -272,14 +274,24 @@ int bwd_launch(const void* q, const void* k, const void* v, const void* o, const
     args.N = N;
     args.scale = scale;
     args.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+    if (drop) {
+        const int t = drop_threshold(drop->p);
+        args.drop_k0 = static_cast<uint32_t>(drop->seed);
+        args.drop_k1 = static_cast<uint32_t>(drop->seed >> 32);
+        args.drop_offset = drop->offset;
+        args.drop_t = static_cast<uint32_t>(t);
+        args.drop_keep_scale = static_cast<float>(256.0 / (256 - t));
+    }
 
     BwdKernel dkdv, dqk;
     void (*delta_k)(fa::BwdArgs);
     if (d == 64) {
-        pick_bwd<64>(mask_kind, dkdv, dqk);
+        if (drop) pick_bwd<64, true>(mask_kind, dkdv, dqk);
+        else pick_bwd<64, false>(mask_kind, dkdv, dqk);
         delta_k = fa::fa_bwd_delta_kernel<64>;
     } else {
-        pick_bwd<128>(mask_kind, dkdv, dqk);
+        if (drop) pick_bwd<128, true>(mask_kind, dkdv, dqk);
+        else pick_bwd<128, false>(mask_kind, dkdv, dqk);
         delta_k = fa::fa_bwd_delta_kernel<128>;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -502,6 +514,15 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const int32_t* seqlens, int in_dtype, int grad_dtype, void* stream) {
     return bwd_launch(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask_kind, seqlens, in_dtype,
                       grad_dtype, stream);
+}
+
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int mask_kind,
+                   const int32_t* seqlens, float p_drop, uint64_t seed, uint32_t offset, int in_dtype, int grad_dtype,
+                   void* stream) {
+    const DropSpec drop{p_drop, seed, offset};
+    return bwd_launch(q, k, v, o, lse, dout, delta, dq, dk, dv, B, H, N, d, scale, mask_kind, seqlens, in_dtype,
+                      grad_dtype, stream, &drop);
 }
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,

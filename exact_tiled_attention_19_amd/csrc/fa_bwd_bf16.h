@@ -29,6 +29,7 @@
 #pragma once
 
 #include "fa_fwd_bf16.h"
+#include "fa_dropout.h"
 
 namespace fa {
 
@@ -47,6 +48,10 @@ struct BwdArgs {
     int B, H, N;
     float scale;             // multiplier of the raw dot products
     float scale_log2;        // scale * log2(e)
+    // dropout of the forward pass (kernels instantiated with dropout only; contract of
+    // fa_fwd_dropout): dV = (P Z)^T dO, dP = Z (dO V^T), with Z = keep * keep_scale
+    uint32_t drop_k0, drop_k1, drop_offset, drop_t;
+    float drop_keep_scale;
 };
 
 constexpr float kLog2e = 1.4426950408889634074f;
@@ -136,7 +141,7 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
 template <int D, bool CAUSAL>
 constexpr int bwd_bq() { return D == 128 && CAUSAL ? 64 : 32; }
 
-template <int D, bool CAUSAL, bool PAD>
+template <int D, bool CAUSAL, bool PAD, bool DROP = false>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int BK = 128;        // keys per workgroup (32 per wave)
     constexpr int BQ = bwd_bq<D, CAUSAL>();  // query rows per tile, handled as 32-row halves
@@ -250,6 +255,9 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
         auto half = [&](int h, auto masked_c) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_c)::value;
             u32x4 ph[2], dsh[2];
+            uint32_t kbits = 0;   // dropout: bit 4 (r / 4) + r % 4 set iff element r is kept
+            if constexpr (DROP)
+                kbits = dropout_bits_kmajor(key, r0 + 32 * h, hh, bh, a.drop_offset, a.drop_k0, a.drop_k1, a.drop_t);
 #pragma unroll
             for (int r = 0; r < 16; r += 4) {
                 const int rr = 32 * h + 8 * (r >> 2) + 4 * hh;       // rows rr .. rr+3
@@ -264,8 +272,15 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
                         const bool ok = g < N && key < Lk && (!CAUSAL || key <= g);
                         e = ok ? e : 0.f;
                     }
-                    p[u] = e;
-                    ds[u] = e * (dp[h][r + u] - d4[u]);
+                    if constexpr (DROP) {
+                        // dV takes P Z (Z's scale applied to dV at the end), dS = P (Z dP~ - D)
+                        const bool keep = (kbits >> (r + u)) & 1u;
+                        p[u] = keep ? e : 0.f;
+                        ds[u] = e * ((keep ? a.drop_keep_scale * dp[h][r + u] : 0.f) - d4[u]);
+                    } else {
+                        p[u] = e;
+                        ds[u] = e * (dp[h][r + u] - d4[u]);
+                    }
                 }
                 ph[r / 8][(r % 8) / 2] = pack_bf16x2(p[0], p[1]);
                 ph[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(p[2], p[3]);
@@ -304,13 +319,14 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
                 const int64_t off = base + (int64_t)key * D + d0;
                 *(f32x4*)(a.dk + off) = f32x4{a.scale * dkt[db][4 * jj], a.scale * dkt[db][4 * jj + 1],
                                               a.scale * dkt[db][4 * jj + 2], a.scale * dkt[db][4 * jj + 3]};
-                *(f32x4*)(a.dv + off) = f32x4{dvt[db][4 * jj], dvt[db][4 * jj + 1], dvt[db][4 * jj + 2],
-                                              dvt[db][4 * jj + 3]};
+                const float vs = DROP ? a.drop_keep_scale : 1.f;
+                *(f32x4*)(a.dv + off) = f32x4{vs * dvt[db][4 * jj], vs * dvt[db][4 * jj + 1], vs * dvt[db][4 * jj + 2],
+                                              vs * dvt[db][4 * jj + 3]};
             }
     }
 }
 
-template <int D, bool CAUSAL, bool PAD>
+template <int D, bool CAUSAL, bool PAD, bool DROP = false>
 __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArgs a) {
     constexpr int BM = 128;        // query rows per workgroup (32 per wave)
     constexpr int BN = 64;         // keys per tile
@@ -406,6 +422,8 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
         auto block = [&](int kb, auto masked_c) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_c)::value;
             u32x4 dsh[2];
+            uint32_t dw[4];   // dropout words of this 32-key block (forward layout)
+            if constexpr (DROP) dropout_words_fwd(dw, j0, kb, row, hh, bh, a.drop_offset, a.drop_k0, a.drop_k1);
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 float ds[2];
@@ -417,7 +435,12 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
                         const bool ok = key < Lk && (!CAUSAL || key <= row);
                         e = ok ? e : 0.f;
                     }
-                    ds[u] = e * (dp[kb][r + u] - dl);
+                    if constexpr (DROP) {
+                        const bool keep = drop_keep(dw[(r + u) >> 2], (r + u) & 3, a.drop_t);
+                        ds[u] = e * ((keep ? a.drop_keep_scale * dp[kb][r + u] : 0.f) - dl);
+                    } else {
+                        ds[u] = e * (dp[kb][r + u] - dl);
+                    }
                 }
                 dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
             }

@@ -63,6 +63,34 @@ __device__ __forceinline__ void dropout_words_fwd(uint32_t (&out)[4], int kv0, i
     out[3] = pick(quad_bcast<3>(w[0]), quad_bcast<3>(w[1]), quad_bcast<3>(w[2]), quad_bcast<3>(w[3]));
 }
 
+// Keep bits of one 32-row half of a dK/dV tile, key-major layout: the lane owns key `key`
+// (key mod 4 = its position a in the quad of lanes holding keys 4m .. 4m+3) and rows
+// rbase + 8 q + 4 hh + u (q, u in 0..3).  Rows rbase + 8 q + 4 hh .. +3 form block (key / 4,
+// (rbase + 8 q + 4 hh) / 4), whose word u holds row u and whose byte a holds this key; the quad
+// needs the same four blocks, so lane a computes block q = a and the quad exchanges the words.
+// Bit 4 q + u of the result: is (row rbase + 8 q + 4 hh + u, key) kept?
+__device__ __forceinline__ uint32_t dropout_bits_kmajor(int key, int rbase, int hh, int bh, uint32_t offset,
+                                                        uint32_t k0, uint32_t k1, uint32_t t) {
+    const int a = key & 3;
+    const u32x4 w = philox4x32_10((uint32_t)key >> 2, (uint32_t)(rbase + 8 * a + 4 * hh) >> 2, (uint32_t)bh, offset,
+                                  k0, k1);
+    uint32_t bits = 0;
+    auto add = [&](uint32_t x, int bit) __attribute__((always_inline)) {
+        bits |= (((x >> (8 * a)) & 0xFFu) >= t ? 1u : 0u) << bit;
+    };
+#define FA_DROP_KM(Q)                        \
+    add(quad_bcast<Q>(w[0]), 4 * (Q) + 0);   \
+    add(quad_bcast<Q>(w[1]), 4 * (Q) + 1);   \
+    add(quad_bcast<Q>(w[2]), 4 * (Q) + 2);   \
+    add(quad_bcast<Q>(w[3]), 4 * (Q) + 3);
+    FA_DROP_KM(0)
+    FA_DROP_KM(1)
+    FA_DROP_KM(2)
+    FA_DROP_KM(3)
+#undef FA_DROP_KM
+    return bits;
+}
+
 // Is byte b of word w at least the threshold (element kept)?
 __device__ __forceinline__ bool drop_keep(uint32_t w, int b, uint32_t t) { return ((w >> (8 * b)) & 0xFFu) >= t; }
 

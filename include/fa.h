@@ -213,6 +213,21 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  */
 size_t fa_fwd_varlen_workspace_size(int B, int H, int max_seqlen_q, int max_seqlen_k, int d);
 
+/*
+ * fa_bwd_dropout -- gradients of fa_fwd_dropout's output with respect to Q, K and V, with the
+ * dropout mask of the same (p_drop, seed, offset) regenerated from the contract of
+ * fa_fwd_dropout (no mask is stored):
+ *     dV = (P * Z)^T dO,   dP = Z * (dO V^T),   D_i = dO_i . O_i,   dS = P * (dP - D),
+ *     dQ = scale * dS K,   dK = scale * dS^T Q,   Z = keep * 256 / (256 - round(256 p_drop)).
+ * o must be fa_fwd_dropout's output and lse its LSE.  Arguments, layouts and validation as for
+ * fa_bwd, plus p_drop, seed and offset as for fa_fwd_dropout.
+ */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, float* delta, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
+                   float p_drop, uint64_t seed, uint32_t offset,
+                   int in_dtype, int grad_dtype, void* stream);
+
 /* Number of kernel variants fa_fwd_variant accepts (variants are 0 .. count-1). */
 int fa_variant_count(void);
 
