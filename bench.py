@@ -341,9 +341,11 @@ def main() -> int:
         grads = tuple(torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
         delta = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
 
+        drop = None if args.dropout is None else (args.dropout, 1234, 0)   # the forward's mask
+
         def step():
             fa.backward(q, k, v, o, lse, dout, scale=x.scale, causal=causal, seqlens=seq, out=grads,
-                        delta=delta)
+                        delta=delta, dropout=drop)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
