@@ -44,7 +44,7 @@ PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILES = os.path.join(ROOT, "profiles", "*_traffic.txt")
 KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h",
-                  "fa_decode_bf16.h"]
+                  "fa_decode_bf16.h", "fa_dropout.h", "fa_bwd_bf16.h"]
 
 
 def kernel_source_hash() -> str:
