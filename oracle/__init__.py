@@ -10,4 +10,5 @@ from .attention_varlen import attention_varlen_ref, brute_varlen_ref, causal_off
 from .attention_dropout import (attention_dropout_ref, attention_dropout_bwd_ref, dropout_threshold,  # noqa: F401
                                 keep_mask, keep_mask_loop, _philox_np)
 from .philox import philox4x32  # noqa: F401
+from .attention_fp8 import attention_fp8_ref, dequantize, e4m3_decode  # noqa: F401
 from . import accounting  # noqa: F401
