@@ -41,6 +41,10 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s and % of bf16 MFMA peak, N=4k–128k, d=64/128, 1 GPU"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 PEAK_F32_TFLOPS = 157.3     # MI355X dense fp32 MFMA
+PEAK_FP8_TFLOPS = 5033.2    # MI355X dense fp8 MFMA: 256 CU x 8192 FLOP/clk x 2.4 GHz
+# 8-bit inputs: S = Q K^T (half the counted FLOP) runs on fp8 MFMA, O += P V (the other half) on
+# bf16 MFMA, so the time at peak is F/2 / fp8 peak + F/2 / bf16 peak
+PEAK_FP8_BF16_MIXED_TFLOPS = round(1.0 / (0.5 / PEAK_FP8_TFLOPS + 0.5 / PEAK_BF16_TFLOPS), 1)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILES = os.path.join(ROOT, "profiles", "*_traffic.txt")
 KERNEL_SOURCES = ["fa_api.hip", "fa_fwd_bf16.h", "fa_fwd_bf16_pipe.h", "fa_fwd_f32.h", "fa_sched.h",
@@ -206,8 +210,9 @@ def bench_packed(args, w) -> int:
     return 0
 
 
-def cpu_baseline(w, x, rows_per_head: int):
-    """Time the fp64 oracle on `rows_per_head` seed-chosen query rows of every head."""
+def cpu_baseline(w, x, rows_per_head: int, descales=None):
+    """Time the fp64 oracle on `rows_per_head` seed-chosen query rows of every head (8-bit
+    inputs: the 8-bit oracle with the given descales)."""
     import numpy as np  # noqa: F401
     import torch
     import oracle
@@ -223,7 +228,10 @@ def cpu_baseline(w, x, rows_per_head: int):
     causal = bool(w.mask_kinds[0] & 1)
     seq = x.seqlens.tolist() if x.seqlens is not None else None
     t0 = time.perf_counter()
-    oracle.attention_ref(x.q, x.k, x.v, x.scale, causal=causal, seqlens=seq, rows=rows)
+    if descales is None:
+        oracle.attention_ref(x.q, x.k, x.v, x.scale, causal=causal, seqlens=seq, rows=rows)
+    else:
+        oracle.attention_fp8_ref(x.q, x.k, x.v, *descales, x.scale, causal=causal, seqlens=seq, rows=rows)
     dt = time.perf_counter() - t0
     # counted FLOP of the sampled rows: each row carries 4*d*(keys it is charged for); the
     # causal convention charges a row N/2 keys on average, so a uniform sample of R rows per
@@ -276,6 +284,9 @@ def main() -> int:
     ap.add_argument("--dropout", type=float, default=None,
                     help="time the forward with dropout of this probability on the attention weights "
                          "(fa_fwd_dropout, Philox seed 1234)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 E4M3 inputs (fa_fwd_fp8): the workload's normals quantised per tensor "
+                         "with amax descales")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (fa_bwd: dQ, dK, dV) instead of the forward")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -313,6 +324,13 @@ def main() -> int:
         w = dataclasses.replace(w, qk_gain=args.qk_gain)
     x = W.make_inputs(w, mask_kind=mask)
     dev = torch.device("cuda", 0)
+    if args.fp8 and (args.bwd or args.dropout is not None or probe or w.in_dtype != torch.bfloat16):
+        print("bench.py: --fp8 times the forward of a bf16 workload (c1..c4), without --bwd or --dropout",
+              file=sys.stderr)
+        return 1
+    if args.fp8:
+        q8, k8, v8, descales = W.random_qkv_fp8(w.B, w.H, w.N, w.d, w.seed, w.qk_gain)
+        x = dataclasses.replace(x, q=q8, k=k8, v=v8)
     q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
     seq = x.seqlens.to(dev) if (mask & W.MASK_KEY_PADDING) else None
     o = torch.empty(q.shape, dtype=out_dtype, device=dev)
@@ -322,6 +340,11 @@ def main() -> int:
     def step():
         fa.forward(q, k, v, scale=x.scale, causal=causal, seqlens=seq, out_dtype=out_dtype,
                    out=o, lse_out=lse, variant=args.variant)
+
+    if args.fp8:
+        def step():
+            fa.forward_fp8(q, k, v, descale_q=descales[0], descale_k=descales[1], descale_v=descales[2],
+                           scale=x.scale, causal=causal, seqlens=seq, out_dtype=out_dtype, out=o, lse_out=lse)
 
     if args.dropout is not None:
         def step():
@@ -373,15 +396,17 @@ def main() -> int:
         flops *= 2.5
     value = flops / (wall / args.steps) / 1e12
     fp32 = w.in_dtype == torch.float32
-    nbytes = compulsory_bytes(w.B, w.H, w.N, w.d, 4 if fp32 else 2, 4 if out_dtype == torch.float32 else 2)
+    nbytes = compulsory_bytes(w.B, w.H, w.N, w.d, 4 if fp32 else 1 if args.fp8 else 2,
+                              4 if out_dtype == torch.float32 else 2)
     if probe:   # HBM-bound: compulsory bytes per launch against the HBM peak
         bound, unit, peak, achieved = "hbm", "GB/s", PEAK_HBM_GBS, nbytes / avg_launch_s / 1e9
     else:       # MFMA-bound: counted FLOP per launch against the dense MFMA peak of the input dtype
         bound, unit = "mfma", "TFLOP/s"
-        peak = PEAK_F32_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+        peak = PEAK_F32_TFLOPS if fp32 else PEAK_FP8_BF16_MIXED_TFLOPS if args.fp8 else PEAK_BF16_TFLOPS
         achieved = flops / avg_launch_s / 1e12
     mask_name = {0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[mask]
-    workload_id = f"{w.name}:{mask_name}:{'f32' if out_dtype == torch.float32 else 'bf16'}-out"
+    workload_id = (f"{w.name}:{mask_name}:{'fp8-in:' if args.fp8 else ''}"
+                   f"{'f32' if out_dtype == torch.float32 else 'bf16'}-out")
     traffic = recorded_traffic(workload_id)
 
     res = {
@@ -396,12 +421,12 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if fp32 else "bf16",
+        "dtype": "f32" if fp32 else "fp8-e4m3 (Q K^T), bf16 (P V)" if args.fp8 else "bf16",
         "data": "synthetic (seeded normal Q, K, V of the workload's shape; no dataset)",
         "config": {
             "workload": (f"{w.name}: B={w.B} H={w.H} N={w.N} d={w.d} {mask_name} mask, "
                          + (f"Q/K gain {w.qk_gain:g}, " if w.qk_gain != 1.0 else "")
-                         + f"{'fp32' if fp32 else 'bf16'} in, "
+                         + f"{'fp32' if fp32 else 'fp8 e4m3 (per-tensor descales)' if args.fp8 else 'bf16'} in, "
                          + f"{'fp32' if out_dtype == torch.float32 else 'bf16'} out, fp32 LSE"),
             "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask_name,
             "flop_per_step": flops, "compulsory_bytes_per_step": nbytes, "variant": args.variant,
@@ -424,7 +449,7 @@ def main() -> int:
         res["roofline"]["traffic"] = None
     if not args.no_cpu_baseline and not args.bwd and args.dropout is None:
         print(f"[bench] timing the fp64 oracle on {args.cpu_rows} rows per head", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_rows, w.N))
+        res["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_rows, w.N), descales if args.fp8 else None)
     print(json.dumps(res), flush=True)
     return 0
 

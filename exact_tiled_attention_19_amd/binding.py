@@ -28,6 +28,7 @@ FA_MASK_KEY_PADDING = 2
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_FP8_E4M3 = 2
 
 FA_ALIGN_BOTTOM_RIGHT = 0
 FA_ALIGN_TOP_LEFT = 1
@@ -40,6 +41,8 @@ _VP = ctypes.c_void_p
 _I = ctypes.c_int
 SIGNATURES = {
     "fa_fwd": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP]),
+    "fa_fwd_fp8": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                        ctypes.c_float, _I, _VP, _I, _VP]),
     "fa_fwd_variant": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, _I, _I, _VP, _I]),
     "fa_fwd_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP, ctypes.c_float,
                             ctypes.c_uint64, ctypes.c_uint32, _I, _I, _VP]),
@@ -173,6 +176,57 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
                 _ptr(seqlens), _DTYPE_CODE[q.dtype], _DTYPE_CODE[out_dtype], stream, variant)
     _check(st)
     return out, lse
+
+
+def fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, descale_q, descale_k, descale_v, mask_kind, seqlens, out_dtype,
+               stream) -> int:
+    """Raw call of the 8-bit-input forward through the C ABI (pointers as ints or None)."""
+    f = ctypes.c_float
+    return load_library().fa_fwd_fp8(q, k, v, o, lse, B, H, N, d, f(scale), f(descale_q), f(descale_k), f(descale_v),
+                                     mask_kind, seqlens, out_dtype, stream)
+
+
+_FP8_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def forward_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, descale_q: float = 1.0,
+                descale_k: float = 1.0, descale_v: float = 1.0, scale: Optional[float] = None,
+                causal: bool = False, seqlens: Optional[torch.Tensor] = None,
+                out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+                lse_out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Attention forward on FP8 E4M3 inputs (contract in include/fa.h): returns (O, LSE).
+
+    q, k, v: [B, H, N, d] contiguous device tensors of E4M3 codes (torch.uint8 or
+    torch.float8_e4m3fn); the real inputs are descale_* times the decoded codes.
+    """
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k, v must be device tensors")
+    if any(t.dtype not in _FP8_DTYPES for t in (q, k, v)):
+        raise ValueError("q, k, v must hold E4M3 codes (uint8 or float8_e4m3fn)")
+    if q.dim() != 4 or q.shape != k.shape or q.shape != v.shape or not all(t.is_contiguous() for t in (q, k, v)):
+        raise ValueError("q, k, v must all be contiguous [B, H, N, d]")
+    B, H, N, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    if out_dtype not in _DTYPE_CODE:
+        raise ValueError("out_dtype must be bfloat16 or float32")
+    mask = FA_MASK_CAUSAL if causal else FA_MASK_NONE
+    if seqlens is not None:
+        if not seqlens.is_cuda or seqlens.dtype != torch.int32 or seqlens.numel() != B or not seqlens.is_contiguous():
+            raise ValueError("seqlens must be a contiguous int32 device tensor with B entries")
+        mask |= FA_MASK_KEY_PADDING
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
+    elif out.shape != q.shape or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if lse_out is None:
+        lse_out = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse_out.shape != (B, H, N) or lse_out.dtype != torch.float32 or not lse_out.is_contiguous():
+        raise ValueError("lse_out must be a contiguous float32 [B, H, N] tensor")
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse_out), B, H, N, d, float(scale), float(descale_q),
+                    float(descale_k), float(descale_v), mask, _ptr(seqlens), _DTYPE_CODE[out_dtype], stream)
+    _check(st)
+    return out, lse_out
 
 
 def fa_fwd_dropout(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, p_drop, seed, offset, in_dtype, out_dtype,

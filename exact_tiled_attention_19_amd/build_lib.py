@@ -13,14 +13,14 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
-SOURCES = ["fa_api.hip"]
+SOURCES = ["fa_api.hip", "fa_fp8.hip"]
+OBJ_DIR = os.path.join(PKG_DIR, "_build")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++20",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU instructions stay off in every HIP build of this project
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
@@ -35,20 +35,40 @@ def hipcc() -> str:
     return path
 
 
+def _clean(stderr: str) -> str:
+    # the host pass does not know the packed-fp32 feature and says so; that line is noise
+    noise = "is not a recognized feature for this target"
+    return "\n".join(l for l in (stderr or "").splitlines() if noise not in l)
+
+
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    """Compile every source to an object (in parallel), then link libfa.so."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *HIPCC_FLAGS, "-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        objs.append(obj)
+    failed = []
+    for src, p in procs:
+        _, err = p.communicate()
+        err = _clean(err)
+        if p.returncode != 0:
+            failed.append(f"{src} ({p.returncode}):\n{err}")
+        elif verbose and err.strip():
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("hipcc failed: " + "\n".join(failed))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *srcs]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    # the host pass does not know the packed-fp32 feature and says so; that line is noise
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"hipcc link failed ({r.returncode}):\n{_clean(r.stderr)}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

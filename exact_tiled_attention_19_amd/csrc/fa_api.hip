@@ -104,18 +104,28 @@ Launch pick_bf16_drop(int mask) {
 
 int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
            int d, float scale, int mask_kind, const int32_t* seqlens, int in_dtype, int out_dtype,
-           void* stream, int variant, const DropSpec* drop = nullptr) {
+           void* stream, int variant, const DropSpec* drop = nullptr, const float* descale = nullptr) {
     // ---- validation (host only, before any HIP call) ----
     if (B < 0 || H < 0 || N < 0) return FA_ERR_INVALID_ARG;
     if (mask_kind < 0 || mask_kind > (FA_MASK_CAUSAL | FA_MASK_KEY_PADDING)) return FA_ERR_INVALID_ARG;
     if (!std::isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
-    if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
+    if (in_dtype != FA_DTYPE_F32 && in_dtype != FA_DTYPE_BF16 && in_dtype != FA_DTYPE_FP8_E4M3) return FA_ERR_INVALID_ARG;
+    const bool f8 = in_dtype == FA_DTYPE_FP8_E4M3;
+    // 8-bit inputs: per-tensor descales (Q, K, V); Q's and K's fold into the score multiplier
+    const double dq = f8 && descale ? descale[0] : 1.0, dk = f8 && descale ? descale[1] : 1.0;
+    const double dv = f8 && descale ? descale[2] : 1.0;
+    if (!std::isfinite(dq) || !std::isfinite(dk) || !std::isfinite(dv) || dq < 0 || dk < 0 || dv < 0)
+        return FA_ERR_INVALID_ARG;
+    const double eff_scale = static_cast<double>(scale) * dq * dk;
+    if (!std::isfinite(static_cast<float>(eff_scale)) || !std::isfinite(static_cast<float>(eff_scale * 1.4426950408889634074)))
+        return FA_ERR_INVALID_ARG;
     if (out_dtype != FA_DTYPE_F32 && out_dtype != FA_DTYPE_BF16) return FA_ERR_INVALID_ARG;
     if (d <= 0) return FA_ERR_INVALID_ARG;
     if (variant < 0 || variant >= kNumVariants) return FA_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_DTYPE_F32 && out_dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
     if (in_dtype == FA_DTYPE_F32 && variant != 0) return FA_ERR_UNSUPPORTED;
+    if (f8 && variant != 0) return FA_ERR_UNSUPPORTED;
     if (variant == 3 && d != 128) return FA_ERR_UNSUPPORTED;
     if (drop && drop_threshold(drop->p) < 0) return FA_ERR_INVALID_ARG;
     if (drop && in_dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
@@ -135,6 +145,12 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
         const bool of32 = out_dtype == FA_DTYPE_F32;
         if (d == 64) L = of32 ? pick_bf16_drop<64, true>(mask_kind) : pick_bf16_drop<64, false>(mask_kind);
         else L = of32 ? pick_bf16_drop<128, true>(mask_kind) : pick_bf16_drop<128, false>(mask_kind);
+    } else if (f8) {
+        const bool wide = d == 128 && (mask_kind & FA_MASK_CAUSAL) &&
+                          static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 255) / 256) >= kWave8MinTiles;
+        int bm = 0, threads = 0;
+        const Kernel kern = fa::pick_fp8_kernel(d, mask_kind, out_dtype == FA_DTYPE_F32, wide, &bm, &threads);
+        L = {kern, bm, true, threads};
     } else if (in_dtype == FA_DTYPE_BF16) {
         const bool of32 = out_dtype == FA_DTYPE_F32;
         if (d == 64) L = of32 ? pick_bf16_mask<64, true>(mask_kind, variant) : pick_bf16_mask<64, false>(mask_kind, variant);
@@ -145,13 +161,14 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
 
     // sizes: element offsets are 64-bit in the kernels; workgroup counts and per-head byte
     // sizes (buffer resources) must fit in 32 bits
+    if (!L.kern || L.bm <= 0) return FA_ERR_UNSUPPORTED;
     const int64_t n_qtiles = (static_cast<int64_t>(N) + L.bm - 1) / L.bm;
     const bool causal = (mask_kind & FA_MASK_CAUSAL) != 0;
     const int64_t n_items = (L.paired && causal) ? (n_qtiles + 1) / 2 : n_qtiles;
     const int64_t total = static_cast<int64_t>(B) * H * n_items;
     if (total > 0x7fffffff || static_cast<int64_t>(B) * H > 0x7fffffff) return FA_ERR_INVALID_ARG;
     if (static_cast<int64_t>(N) * d * 4 > 0x7fffffff) return FA_ERR_INVALID_ARG;
-    const size_t in_bytes = static_cast<size_t>(B) * H * N * d * (in_dtype == FA_DTYPE_F32 ? 4 : 2);
+    const size_t in_bytes = static_cast<size_t>(B) * H * N * d * (in_dtype == FA_DTYPE_F32 ? 4 : f8 ? 1 : 2);
     const size_t out_bytes = static_cast<size_t>(B) * H * N * d * (out_dtype == FA_DTYPE_F32 ? 4 : 2);
     if (overlaps(o, out_bytes, q, in_bytes) || overlaps(o, out_bytes, k, in_bytes) ||
         overlaps(o, out_bytes, v, in_bytes))
@@ -182,8 +199,9 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     args.N = N;
     args.n_qtiles = static_cast<int>(n_qtiles);
     args.total_wgs = static_cast<int>(total);
-    args.scale = scale;
-    args.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
+    args.scale = static_cast<float>(eff_scale);
+    args.scale_log2 = static_cast<float>(eff_scale * 1.4426950408889634074);
+    args.v_descale = static_cast<float>(dv);
 
     if (!L.kern) return FA_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(L.kern, dim3(static_cast<unsigned>(total)), dim3(L.threads), 0,
@@ -536,6 +554,14 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
                    int in_dtype, int out_dtype, void* stream) {
     const DropSpec drop{p_drop, seed, offset};
     return launch(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, in_dtype, out_dtype, stream, 0, &drop);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, float descale_q, float descale_k, float descale_v, int mask_kind, const int32_t* seqlens,
+               int out_dtype, void* stream) {
+    const float descale[3] = {descale_q, descale_k, descale_v};
+    return launch(q, k, v, o, lse, B, H, N, d, scale, mask_kind, seqlens, FA_DTYPE_FP8_E4M3, out_dtype, stream, 0,
+                  nullptr, descale);
 }
 
 int fa_fwd_variant(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

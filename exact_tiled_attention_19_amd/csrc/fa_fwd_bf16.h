@@ -65,7 +65,17 @@ struct FwdArgs {
     uint32_t drop_offset;        // fourth Philox counter word
     uint32_t drop_t;             // byte threshold round(256 p): kept iff byte >= drop_t
     float drop_keep_scale;       // 256 / (256 - drop_t)
+    // 8-bit inputs only: the value tensor's descale, applied to the output
+    float v_descale;
 };
+
+using FwdKernelFn = void (*)(FwdArgs);
+
+// The forward kernel for FP8 E4M3 inputs (fa_fp8.hip) for head width d, mask bits `mask` and
+// output type; `wide` asks for the eight-wave 256-row workgroup where one exists.  Sets the
+// query rows per tile (*bm) and threads per workgroup; nullptr when d has no kernel.
+__attribute__((visibility("hidden"))) FwdKernelFn pick_fp8_kernel(int d, int mask, bool out_f32, bool wide, int* bm,
+                                                                  int* threads);
 
 // Where the rows of one head of one sequence live, and which keys its queries may see.
 struct SeqGeom {

@@ -57,6 +57,32 @@ __device__ __forceinline__ int swz_v(int row) {
     return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
 }
 
+// Swizzle of the 16-byte chunks of an 8-bit K row (D bytes): a lane reads 32 bytes (two
+// chunks) of row l32 per k-step; rows 0..7 then start on distinct LDS bank groups.
+template <int D>
+__device__ __forceinline__ int swz_k8(int row) {
+    return D == 128 ? (row & 7) : ((row >> 2) & 3);
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ u32x8 u32x8_of(u32x4 lo, u32x4 hi) { return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7); }
+
+// One S-product step: 32 keys x 32 query rows over 16 (bf16) or 64 (FP8 E4M3) head dimensions.
+// The 8-bit form is v_mfma_f32_32x32x64_f8f6f4 (operand formats 0 = E4M3, block scales off).
+__device__ __forceinline__ f32x16 mfma_s(bf16x8 kf, bf16x8 qf, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma_s(i32x8 kf, i32x8 qf, f32x16 c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Four E4M3 codes (one dword) -> four bf16 (two dwords); every E4M3 value is a bf16 value.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
+    return u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true))};
+}
+
 // IEEE maximum without the canonicalising moves fmaxf needs (v_maximum3_f32 on gfx950).  The
 // scores reduced with it are finite or -inf, so NaN handling does not arise.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
@@ -86,29 +112,34 @@ __device__ __forceinline__ unsigned char* pipe_lds() {
 // dropout on the probabilities that enter the value product (the row sums, and so O's
 // normaliser and the log-sum-exp, take them undropped; kept ones are scaled in the epilogue).
 template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false, int NW = 4,
-          bool DROP = false>
+          bool DROP = false, bool F8 = false>
 __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, const SeqGeom& sg = SeqGeom{}) {
     constexpr int WR = 32 * RB;             // query rows per wave
     constexpr int BM = NW * WR;             // query rows per workgroup
-    constexpr int KC = D / 16;              // k-steps of the S MFMA
+    constexpr int KC = F8 ? D / 64 : D / 16;  // k-steps of the S MFMA
     constexpr int NKB = BN / 32;            // 32-key blocks per tile
     constexpr int NDB = D / 32;             // 32-wide output blocks
     constexpr int PC = BN / 16;             // k-steps of the PV MFMA
-    constexpr int ROWB = D * 2;             // bytes per K/V row in LDS (no padding)
-    constexpr int TILEB = BN * ROWB;        // bytes per K or V tile
-    constexpr int CPR = D / 8;              // 16-byte chunks per row
-    constexpr int LPW = TILEB / 1024 / NW;  // direct-to-LDS instructions per wave per tile
+    constexpr int ESZ = F8 ? 1 : 2;         // bytes per input element
+    constexpr int KROWB = D * ESZ;          // bytes per K row in LDS (no padding)
+    constexpr int ROWB = D * 2;             // bytes per V row in LDS (bf16; 8-bit V is widened)
+    constexpr int KTILEB = BN * KROWB;      // bytes per K tile
+    constexpr int TILEB = BN * ROWB;        // bytes per V tile
+    constexpr int CPR = KROWB / 16;         // 16-byte chunks per input row
+    constexpr int LPW = KTILEB / 1024 / NW; // 1 KiB loads per wave per K (and per V) tile
+    using KFrag = std::conditional_t<F8, i32x8, bf16x8>;   // S operand fragment
     constexpr bool PRECISE = OUT_F32;
     // Shift threshold (log2 units).  With a bf16 output the probabilities enter the PV product
     // as single bf16 values, so the shift tracks the exact row maximum (threshold 0: the largest
     // probability is then exactly 1 and carries no rounding); with the two-term split used for
     // a float32 output a shift lagging by up to 8 costs nothing.
     constexpr float kTau = PRECISE ? 8.0f : 0.0f;
-    static_assert(LPW >= 1 && LPW * NW * 1024 == TILEB, "tile must split into 1 KiB pieces");
+    static_assert(LPW >= 1 && LPW * NW * 1024 == KTILEB, "tile must split into 1 KiB pieces");
+    static_assert(!F8 || (!DROP && !VL && RB == 1), "8-bit inputs: fixed-length heads without dropout");
     static_assert(!DROP || (RB == 1 && BN == 64 && !VL), "dropout words are laid out for one 32-row block");
 
-    unsigned char* const kbuf0 = pipe_lds<TILEB, 0>();
-    unsigned char* const kbuf1 = pipe_lds<TILEB, 1>();
+    unsigned char* const kbuf0 = pipe_lds<KTILEB, 0>();
+    unsigned char* const kbuf1 = pipe_lds<KTILEB, 1>();
     unsigned char* const vbuf0 = pipe_lds<TILEB, 2>();
     unsigned char* const vbuf1 = pipe_lds<TILEB, 3>();
     constexpr int KB0 = 0, KB1 = 1, VB0 = 2, VB1 = 3;
@@ -134,7 +165,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     const int64_t kbase = VL ? sg.kbase : base;                       // key / value rows
     const int64_t lbase = VL ? sg.lbase : (int64_t)tc.bh * N;         // log-sum-exp entries
     const int RSE = VL ? sg.rse : D;           // elements between consecutive rows
-    const int RSB = RSE * 2;                   // the same in bytes
+    const int RSB = RSE * ESZ;                 // the same in bytes (inputs)
     const int dlt = VL ? sg.dlt : 0;           // causal: key j visible to row i iff j <= i + dlt
 
     int Lk = N;
@@ -201,7 +232,23 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     }
 
     // Q^T operand fragments (B operand of the S MFMA), kept in VGPRs for the whole kernel
-    bf16x8 qf[RB][KC];
+    KFrag qf[RB][KC];
+    if constexpr (F8) {
+        // the same byte -> dimension assignment as the K fragments below: lane half hh takes
+        // bytes 64c + 32hh .. 64c + 32hh + 31 of its row in k-step c; the MFMA sums over all
+        // 64 positions of a step whatever its internal order, so Q and K need only agree
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const unsigned char* qp = (const unsigned char*)a.q + base + (int64_t)(qrow[rb] < N ? qrow[rb] : N - 1) * RSE + 32 * hh;
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const u32x4 lo = *(const u32x4*)(qp + 64 * c);
+                const u32x4 hi = *(const u32x4*)(qp + 64 * c + 16);
+                qf[rb][c] = __builtin_bit_cast(i32x8, u32x8_of(lo, hi));
+                if (qrow[rb] >= N) qf[rb][c] = KFrag{};
+            }
+        }
+    } else
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow[rb] < N ? qrow[rb] : N - 1) * RSE + 8 * hh;
@@ -217,36 +264,67 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     // lam writes physical chunk p = 64 r + lam, i.e. row p / CPR, chunk p % CPR, and fetches the
     // logical chunk that the swizzle maps there.  The buffer's byte range ends with the last
     // key row, so rows past it read as zeros (for the packed layout: the last row's end).
-    const int64_t krec = VL ? (int64_t)(Lk - 1) * RSB + ROWB : (int64_t)N * ROWB;
+    const int64_t krec = VL ? (int64_t)(Lk - 1) * RSB + KROWB : (int64_t)N * KROWB;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)a.k + kbase), (short)0, (int)(uint32_t)krec, 0x00020000);
+        (void*)((const unsigned char*)a.k + kbase * ESZ), (short)0, (int)(uint32_t)krec, 0x00020000);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const uint16_t*)a.v + kbase), (short)0, (int)(uint32_t)krec, 0x00020000);
-    uint32_t koff[LPW], voff[LPW];
+        (void*)((const unsigned char*)a.v + kbase * ESZ), (short)0, (int)(uint32_t)krec, 0x00020000);
+    // 8-bit V takes a register round trip instead: lane lam loads the 16 codes of chunk p of
+    // the tile (row p / CPR, dimensions 16 (p % CPR) ..), widens them to bf16 and writes the
+    // two bf16 chunks 2 (p % CPR) and 2 (p % CPR) + 1 of that row into the bf16 V layout
+    uint32_t koff[LPW], voff[LPW], vws[LPW];
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
         const int p = (i * NW + wave) * 64 + lane;
         const int row = p / CPR;
         const int pch = p % CPR;
-        koff[i] = row * RSB + (pch ^ swz_k<D>(row)) * 16;
-        voff[i] = row * RSB + (pch ^ swz_v<D>(row)) * 16;
+        koff[i] = row * RSB + (pch ^ (F8 ? swz_k8<D>(row) : swz_k<D>(row))) * 16;
+        voff[i] = row * RSB + (F8 ? pch : (pch ^ swz_v<D>(row))) * 16;
+        vws[i] = row * ROWB + ((2 * pch) ^ swz_v<D>(row)) * 16;   // chunk 2 pch + 1 follows it
     }
+    auto store_v8 = [&](const u32x4 (&raw)[LPW], int vbuf_id) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const u32x2 w0 = e4m3x4_to_bf16(raw[i][0]), w1 = e4m3x4_to_bf16(raw[i][1]);
+            const u32x2 w2 = e4m3x4_to_bf16(raw[i][2]), w3 = e4m3x4_to_bf16(raw[i][3]);
+            *(u32x4*)(buf(vbuf_id) + vws[i]) = u32x4{w0[0], w0[1], w1[0], w1[1]};
+            *(u32x4*)(buf(vbuf_id) + vws[i] + 16) = u32x4{w2[0], w2[1], w3[0], w3[1]};
+        }
+    };
     auto load_tile = [&](auto is_v, int tile, int buf_off) __attribute__((always_inline)) {
         constexpr bool IS_V = decltype(is_v)::value;
         const uint32_t t0 = (uint32_t)tile * (uint32_t)(BN * RSB);
+        if constexpr (F8 && IS_V) {
+            u32x4 raw[LPW];
 #pragma unroll
-        for (int i = 0; i < LPW; ++i)
-            buffer_load_lds16(IS_V ? vrs : krs, buf(buf_off) + (i * NW + wave) * 1024,
-                              (IS_V ? voff[i] : koff[i]) + t0);
+            for (int i = 0; i < LPW; ++i)
+                raw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i] + t0, 0, 0));
+            store_v8(raw, buf_off);
+        } else {
+#pragma unroll
+            for (int i = 0; i < LPW; ++i)
+                buffer_load_lds16(IS_V ? vrs : krs, buf(buf_off) + (i * NW + wave) * 1024,
+                                  (IS_V ? voff[i] : koff[i]) + t0);
+        }
     };
 
     // ---- LDS read addresses (bytes within a tile buffer) -----------------------------------
     // K operand of k-step c, block kb: row 32kb + l32, logical chunk 2c + hh.
-    const int krow_base = l32 * ROWB;
-    const int kswz = swz_k<D>(l32) * 16;      // 32kb + l32 has the same swizzle as l32
-    int kaddr[KC];                            // byte offset of k-step c's chunk in row l32
+    // 8-bit K: k-step c, lane half hh reads logical chunks 4c + 2hh and 4c + 2hh + 1 (kaddr,
+    // kaddr2), the bytes the Q fragment holds.
+    const int krow_base = l32 * KROWB;
+    const int kswz = (F8 ? swz_k8<D>(l32) : swz_k<D>(l32)) * 16;   // 32kb + l32 has the same swizzle as l32
+    int kaddr[KC], kaddr2[KC];                // byte offset of k-step c's chunk(s) in row l32
 #pragma unroll
-    for (int c = 0; c < KC; ++c) kaddr[c] = krow_base + (((2 * c + hh) * 16) ^ kswz);
+    for (int c = 0; c < KC; ++c) {
+        if constexpr (F8) {
+            kaddr[c] = krow_base + (((4 * c + 2 * hh) * 16) ^ kswz);
+            kaddr2[c] = krow_base + (((4 * c + 2 * hh + 1) * 16) ^ kswz);
+        } else {
+            kaddr[c] = krow_base + (((2 * c + hh) * 16) ^ kswz);
+            kaddr2[c] = kaddr[c];
+        }
+    }
     // V^T operand (transpose read) of chunk pc, block db: row 16pc + 4hh + (l32 & 15) / 4 (+8),
     // logical column 32db + (l32 & 16) + 4 (l32 & 3) -> chunk 4db + ((l32 & 16) >> 3) +
     // ((l32 & 3) >> 1), byte (l32 & 1) * 8 within the chunk.
@@ -260,10 +338,17 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     auto tile_rsrc = [&](const void* t, int64_t off, int tile) __attribute__((always_inline)) {
         const int64_t start = (int64_t)tile * BN * RSB;         // bytes into this head
         const int64_t left = krec - start;
-        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)((const uint16_t*)t + off) + start),
+        return __builtin_amdgcn_make_buffer_rsrc((void*)((const unsigned char*)t + off * ESZ + start),
                                                  (short)0, left > 0 ? (int)(uint32_t)left : 0, 0x00020000);
     };
 
+    auto kfrag_at = [&](int kbuf, int c, int kb) __attribute__((always_inline)) -> KFrag {
+        const unsigned char* p = buf(kbuf) + kb * 32 * KROWB;
+        if constexpr (F8)
+            return __builtin_bit_cast(i32x8, u32x8_of(*(const u32x4*)(p + kaddr[c]), *(const u32x4*)(p + kaddr2[c])));
+        else
+            return *(const bf16x8*)(p + kaddr[c]);
+    };
     auto compute_s = [&](f32x16 (&s)[RB][NKB], int kbuf) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
@@ -271,13 +356,11 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
             for (int kb = 0; kb < NKB; ++kb) s[rb][kb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            const int off = kaddr[c];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 kf = *(const bf16x8*)(buf(kbuf) + off + kb * 32 * ROWB);
+                const KFrag kf = kfrag_at(kbuf, c, kb);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    s[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][c], s[rb][kb], 0, 0, 0);
+                for (int rb = 0; rb < RB; ++rb) s[rb][kb] = mfma_s(kf, qf[rb][c], s[rb][kb]);
             }
         }
     };
@@ -406,10 +489,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     constexpr int EM = NE / HB;             // elements folded into the maximum per slot
     constexpr int NFMA = NPF - HB - 1;      // phase-B slots left for s*c - m
     static_assert(EA * NSF == NE && EM * HB == NE && EA % 2 == 0, "slot split");
+    static_assert(2 * LPW <= NSF, "every K and V load of a tile needs a phase-A slot");
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    auto kfrag = [&](int kbuf, int i) __attribute__((always_inline)) -> bf16x8 {
-        const int c = i / NKB, kb = i % NKB;
-        return *(const bf16x8*)(buf(kbuf) + kaddr[c] + kb * 32 * ROWB);
+    auto kfrag = [&](int kbuf, int i) __attribute__((always_inline)) -> KFrag {
+        return kfrag_at(kbuf, i / NKB, i % NKB);
     };
     auto vfrag = [&](int vbuf, int i) __attribute__((always_inline)) -> bf16x8 {
         const int pc = i / NDB, db = i % NDB;
@@ -446,18 +529,24 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         // dropout words of the current 32-key half of tile j (see dropout_words_fwd)
         uint32_t dw[4];
         // phase A
-        bf16x8 kf = kfrag(KB_OTHER, 0);
-        bf16x8 kf1 = kfrag(KB_OTHER, 1);
+        KFrag kf = kfrag(KB_OTHER, 0);
+        KFrag kf1 = kfrag(KB_OTHER, 1);
+        u32x4 vraw[LPW];   // 8-bit V tile j+1, widened and stored after phase B
 #pragma unroll
         for (int i = 0; i < NSF; ++i) {
             if (i < LPW) buffer_load_lds16(krs_t, buf(KB_THIS) + (i * NW + wave) * 1024, koff[i]);
-            else if (i < 2 * LPW) buffer_load_lds16(vrs_t, buf(VB_OTHER) + ((i - LPW) * NW + wave) * 1024, voff[i - LPW]);
-            bf16x8 kf2 = kf1;           // operands are read two fragments ahead
+            else if (i < 2 * LPW) {
+                if constexpr (F8)
+                    vraw[i - LPW] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs_t, voff[i - LPW], 0, 0));
+                else
+                    buffer_load_lds16(vrs_t, buf(VB_OTHER) + ((i - LPW) * NW + wave) * 1024, voff[i - LPW]);
+            }
+            KFrag kf2 = kf1;            // operands are read two fragments ahead
             if (i + 2 < NSF) kf2 = kfrag(KB_OTHER, i + 2);
             const int c = i / NKB, kb = i % NKB;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                s_nxt[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[rb][c], c == 0 ? f32x16{} : s_nxt[rb][kb], 0, 0, 0);
+                s_nxt[rb][kb] = mfma_s(kf, qf[rb][c], c == 0 ? f32x16{} : s_nxt[rb][kb]);
             if constexpr (DROP) {
                 if ((i * EA) % 16 == 0)   // first slot of a 32-key half
                     dropout_words_fwd(dw, j * BN, (i * EA) / 16, qrow[0], hh, tc.bh, a.drop_offset, a.drop_k0, a.drop_k1);
@@ -565,6 +654,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
             vf1 = vf2;
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (F8) store_v8(vraw, VB_OTHER);   // V_{j+1}: its buffer was last read in j-1
     };
 
     // One pipeline iteration for tile j (parity PAR = j & 1); on entry the score registers of
@@ -588,11 +678,16 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         } else {
             const __amdgpu_buffer_rsrc_t krs_t = tile_rsrc(a.k, kbase, j + 2);
             const __amdgpu_buffer_rsrc_t vrs_t = tile_rsrc(a.v, kbase, j + 1);
+            u32x4 vraw[LPW];
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
                 buffer_load_lds16(krs_t, buf(KB_THIS) + (i * NW + wave) * 1024, koff[i]);
-                buffer_load_lds16(vrs_t, buf(VB_OTHER) + (i * NW + wave) * 1024, voff[i]);
+                if constexpr (F8)
+                    vraw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs_t, voff[i], 0, 0));
+                else
+                    buffer_load_lds16(vrs_t, buf(VB_OTHER) + (i * NW + wave) * 1024, voff[i]);
             }
+            if constexpr (F8) store_v8(vraw, VB_OTHER);
         }
         wait_loads();
         __syncthreads();
@@ -649,7 +744,8 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         // packed sequences under the causal mask: a row may see no key at all (bottom-right
         // alignment with more queries than keys); it gets O = 0 and LSE = -inf
         const bool none = VL && CAUSAL && !(l_tot > 0.f);
-        const float inv_l = none ? 0.f : (DROP ? a.drop_keep_scale : 1.0f) / l_tot;
+        // 8-bit inputs: the value descale multiplies the output (the probabilities never see it)
+        const float inv_l = none ? 0.f : (DROP ? a.drop_keep_scale : F8 ? a.v_descale : 1.0f) / l_tot;
         if (qrow[rb] >= N) continue;
         if (hh == 0 && a.lse) a.lse[lbase + qrow[rb]] = none ? kNegInf : (m_run[rb] + __log2f(l_tot)) * kLn2;
 #pragma unroll
@@ -676,16 +772,17 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 // visible to row i iff j <= i + dlt) -- the first tile of a head, in practice -- and the plain
 // instantiation otherwise, so the diagonal tiles of the long rows pay nothing.  Without the
 // causal mask the only masked tile is the ragged end of the keys, and it always takes them.
-template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL, int NW = 4, bool DROP = false>
+template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL, int NW = 4, bool DROP = false,
+          bool F8 = false>
 __device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int qt, int Lk, int dlt,
                                                    const SeqGeom& sg) {
     constexpr int BM = NW * 32 * RB;
     if constexpr (OUT_F32 || !CAUSAL) {
-        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP>(a, bh, qt, sg);
+        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP, F8>(a, bh, qt, sg);
     } else {
         const bool few = Lk < BN || qt * BM + 1 + dlt < BN;
-        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP>(a, bh, qt, sg);
-        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW, DROP>(a, bh, qt, sg);
+        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP, F8>(a, bh, qt, sg);
+        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW, DROP, F8>(a, bh, qt, sg);
     }
 }
 
@@ -707,6 +804,26 @@ __global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) fa_fwd_bf16_pipe_ker
     if (tp.qt1 >= 0) {
         __syncthreads();   // the first tile's LDS buffers are reused
         pipe_tile_dispatch<D, BN, RB, CAUSAL, PAD, OUT_F32, false, NW, DROP>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
+    }
+}
+
+// FP8 E4M3 inputs ([B, H, N, d] byte tensors, one descale per tensor): the same work items and
+// tile body with S on the 8-bit MFMA (64 head dimensions per step) and V widened to bf16 as it
+// is staged, so the value product, its precision and everything after it are the bf16 path's.
+// The Q and K descales are folded into a.scale / a.scale_log2 by the host; V's into
+// a.v_descale.
+template <int D, int BN, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 4>
+__global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) fa_fwd_fp8_pipe_kernel(FwdArgs a) {
+    const TilePair tp = pair_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
+    int Lk = a.N;
+    if (PAD) {
+        const int s = a.seqlens[tp.bh / a.H];
+        Lk = s < 0 ? 0 : (s > a.N ? a.N : s);
+    }
+    pipe_tile_dispatch<D, BN, 1, CAUSAL, PAD, OUT_F32, false, NW, false, true>(a, tp.bh, tp.qt0, Lk, 0, SeqGeom{});
+    if (tp.qt1 >= 0) {
+        __syncthreads();   // the first tile's LDS buffers are reused
+        pipe_tile_dispatch<D, BN, 1, CAUSAL, PAD, OUT_F32, false, NW, false, true>(a, tp.bh, tp.qt1, Lk, 0, SeqGeom{});
     }
 }
 

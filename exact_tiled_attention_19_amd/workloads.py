@@ -102,6 +102,27 @@ def random_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
     return q.to(dtype), k.to(dtype), v.to(dtype), g
 
 
+def to_e4m3(x: torch.Tensor):
+    """Per-tensor amax quantisation of a float tensor to FP8 E4M3 codes: (uint8 codes, descale).
+
+    descale = max|x| / 448 (as float32; 1 for an all-zero tensor), codes = E4M3 of x / descale
+    rounded to nearest even, clamped to +-448 first.  Input generation only: what the codes
+    mean is fixed by the format, and both sides take them as given.
+    """
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = float(torch.tensor(amax / 448.0 if amax > 0 else 1.0, dtype=torch.float32))
+    y = (x.float() / descale).clamp(-448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).contiguous(), descale
+
+
+def random_qkv_fp8(B: int, H: int, N: int, d: int, seed: int, qk_gain: float = 1.0):
+    """The normals of ``random_qkv`` (same seed, same draw order) quantised per tensor to E4M3:
+    (q8, k8, v8, (descale_q, descale_k, descale_v)), uint8 CPU tensors."""
+    q, k, v, _ = random_qkv(B, H, N, d, torch.float32, seed, qk_gain)
+    (q8, dq), (k8, dk), (v8, dv) = to_e4m3(q), to_e4m3(k), to_e4m3(v)
+    return q8, k8, v8, (dq, dk, dv)
+
+
 def draw_seqlens(g: torch.Generator, B: int, N: int) -> torch.Tensor:
     """One valid key length per batch element, integer uniform on [N/2, N]."""
     return torch.randint(N // 2, N + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)

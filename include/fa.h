@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 10300 /* major*10000 + minor*100 + patch */
+#define FA_VERSION 10400 /* major*10000 + minor*100 + patch */
 
 typedef enum {
     FA_OK = 0,
@@ -55,7 +55,7 @@ typedef enum {
 } fa_status;
 
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_KEY_PADDING = 2 };
-enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1 };
+enum { FA_DTYPE_F32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP8_E4M3 = 2 };
 /* Causal alignment of fa_fwd_varlen (see there). */
 enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 };
 
@@ -76,7 +76,8 @@ enum { FA_ALIGN_BOTTOM_RIGHT = 0, FA_ALIGN_TOP_LEFT = 1 };
  *             (F32, F32) with d in {64, 128}.  Products take bf16 operands with float32
  *             accumulation; with a float32 output the probabilities enter the value product
  *             as a two-term bf16 split, so their rounding stays below 2^-16 relative.
- *             float32 inputs are multiplied in float32 throughout.
+ *             float32 inputs are multiplied in float32 throughout.  FP8_E4M3 inputs (BF16 or
+ *             F32 output): as fa_fwd_fp8 with every descale 1.
  *   stream    hipStream_t to enqueue on (NULL = default stream).
  *
  * Returns an fa_status.
@@ -110,6 +111,32 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, float scale, int mask_kind, const int32_t* seqlens,
                    float p_drop, uint64_t seed, uint32_t offset,
                    int in_dtype, int out_dtype, void* stream);
+
+/*
+ * fa_fwd_fp8 -- fa_fwd for 8-bit floating-point inputs with per-tensor descales:
+ *
+ *     O = softmax(scale * (dq Q)(dk K)^T + mask) (dv V),   LSE as for fa_fwd on those inputs,
+ *
+ * where Q, K and V hold OCP FP8 E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; subnormals; 0x7F and 0xFF are NaN, no infinities; largest finite 448).  The page
+ * "FlashAttention 1, 2 & 3: Memory Tiling & Eliminating the O(N^2) HBM Bottleneck", section 3,
+ * names FP8 support among the third kernel generation's hardware features and fixes nothing
+ * more; the result defined here is exact attention on the real values descale * code.
+ *
+ *   q, k, v   [B, H, N, d] device byte tensors of E4M3 codes, 16-byte aligned.
+ *   descale_q, descale_k, descale_v   finite, >= 0; scale * descale_q * descale_k must be a
+ *             finite float32 (else FA_ERR_INVALID_ARG).
+ *   out_dtype BF16 or F32.  d in {64, 128}.
+ *   Other arguments, layouts, masks and validation as for fa_fwd.
+ *
+ * Q K^T runs on the 8-bit matrix cores with float32 accumulation (exact products); V is
+ * widened to bf16 without rounding, so the value product, the probability precision and the
+ * tolerances are those of fa_fwd with bf16 inputs.  Codes 0x7F / 0xFF (NaN) are outside the
+ * contract, like NaN inputs of fa_fwd.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, float descale_q, float descale_k, float descale_v,
+               int mask_kind, const int32_t* seqlens, int out_dtype, void* stream);
 
 /*
  * fa_fwd_variant -- fa_fwd with an explicit kernel variant, for tests and tuning only.

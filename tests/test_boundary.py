@@ -314,3 +314,38 @@ def test_no_undefined_kernel_symbols():
     host-side instantiation is dropped shows up as an undefined symbol and breaks loading)."""
     out = subprocess.run(["nm", "-D", "--undefined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
     assert not [l for l in out.splitlines() if "fa_fwd" in l or "_ZN2fa" in l], out
+
+
+def fp8_call(dq=1.0, dk=1.0, dv=1.0, outd=BF16, d=64, N=16, **kw):
+    a = dict(q=P, k=P2, v=P3, o=P4, lse=None, B=1, H=1, scale=0.125, mask=0, seqlens=None)
+    a.update(kw)
+    return fa.fa_fwd_fp8(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], N, d, a["scale"], dq, dk, dv,
+                         a["mask"], a["seqlens"], outd, None)
+
+
+FP8_INVALID = {"descale_q nan": dict(dq=float("nan")), "descale_k negative": dict(dk=-1.0),
+               "descale_v inf": dict(dv=float("inf")), "scale * descales overflows float32": dict(dq=1e30, dk=1e30),
+               "null k": dict(k=None), "o aliases v": dict(o=P3), "misaligned q": dict(q=P + 8),
+               "mask bit 4": dict(mask=4), "padding without seqlens": dict(mask=fa.FA_MASK_KEY_PADDING),
+               "unknown out dtype": dict(outd=fa.FA_DTYPE_FP8_E4M3)}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_INVALID))
+def test_fp8_invalid_argument_rejected_on_host(name):
+    assert fp8_call(**FP8_INVALID[name]) == fa.FA_ERR_INVALID_ARG, name
+
+
+def test_fp8_unsupported_and_empty():
+    assert fp8_call(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert fp8_call(d=32) == fa.FA_ERR_UNSUPPORTED
+    assert fp8_call(N=0, q=None, k=None, v=None, o=None) == fa.FA_OK
+    # 8-bit inputs have only the production kernel, and no dropout path
+    assert call(ind=fa.FA_DTYPE_FP8_E4M3, variant=1) == fa.FA_ERR_UNSUPPORTED
+    assert drop_call(ind=fa.FA_DTYPE_FP8_E4M3) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_python_fp8_forward_rejects_bad_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        fa.forward_fp8(x, x, x)
