@@ -125,7 +125,7 @@ __device__ __forceinline__ float xor32_sum(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Round-to-nearest-even float -> bf16 bits (finite inputs; the probabilities are in [0, 1]).
+// Round-to-nearest-even float -> bf16 bits (finite inputs).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     bf16x2 r = {(__bf16)lo, (__bf16)hi};

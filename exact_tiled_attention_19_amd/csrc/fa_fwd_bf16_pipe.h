@@ -58,10 +58,11 @@ __device__ __forceinline__ int swz_v(int row) {
 }
 
 // Swizzle of the 16-byte chunks of an 8-bit K row (D bytes): a lane reads 32 bytes (two
-// chunks) of row l32 per k-step; rows 0..7 then start on distinct LDS bank groups.
+// chunks) of row l32 per k-step.  LDS serves 16-byte reads 16 lanes (256 bytes, all 64 banks)
+// at a time; the 16 rows such a group reads then fall on 16 distinct 16-byte bank groups.
 template <int D>
 __device__ __forceinline__ int swz_k8(int row) {
-    return D == 128 ? (row & 7) : ((row >> 2) & 3);
+    return D == 128 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -282,13 +283,19 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         voff[i] = row * RSB + (F8 ? pch : (pch ^ swz_v<D>(row))) * 16;
         vws[i] = row * ROWB + ((2 * pch) ^ swz_v<D>(row)) * 16;   // chunk 2 pch + 1 follows it
     }
+    // Rows whose starts share LDS banks (256 / ROWB rows apart: the next row at d = 128, the one
+    // after at d = 64) write their two chunks in opposite orders, so that each write of a group
+    // of 16 lanes covers 16 distinct 16-byte bank groups.  Every piece starts on a row that is a
+    // multiple of 8, so the lane alone decides.
+    const bool v8_swap = (((lane / CPR) >> (ROWB == 256 ? 0 : 1)) & 1) != 0;
     auto store_v8 = [&](const u32x4 (&raw)[LPW], int vbuf_id) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
             const u32x2 w0 = e4m3x4_to_bf16(raw[i][0]), w1 = e4m3x4_to_bf16(raw[i][1]);
             const u32x2 w2 = e4m3x4_to_bf16(raw[i][2]), w3 = e4m3x4_to_bf16(raw[i][3]);
-            *(u32x4*)(buf(vbuf_id) + vws[i]) = u32x4{w0[0], w0[1], w1[0], w1[1]};
-            *(u32x4*)(buf(vbuf_id) + vws[i] + 16) = u32x4{w2[0], w2[1], w3[0], w3[1]};
+            const u32x4 lo = u32x4{w0[0], w0[1], w1[0], w1[1]}, hi = u32x4{w2[0], w2[1], w3[0], w3[1]};
+            *(u32x4*)(buf(vbuf_id) + vws[i] + (v8_swap ? 16 : 0)) = v8_swap ? hi : lo;
+            *(u32x4*)(buf(vbuf_id) + vws[i] + (v8_swap ? 0 : 16)) = v8_swap ? lo : hi;
         }
     };
     auto load_tile = [&](auto is_v, int tile, int buf_off) __attribute__((always_inline)) {
@@ -620,7 +627,18 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                 for (int rb = 0; rb < RB; ++rb) {
                     const float m = xor32_max(vmax(mx[rb][0], mx[rb][1]));
                     m_tile[rb] = m * a.scale_log2;
-                    need[rb] = m_tile[rb] > m_run[rb] + kTau;
+                    if constexpr (PRECISE) {
+                        need[rb] = m_tile[rb] > m_run[rb] + kTau;
+                    } else {
+                        // bf16 probabilities: a raised maximum moves the shift (so that the new
+                        // largest probability is exactly 1) unless that probability, 2^(m_tile -
+                        // m_run), is at most a quarter of the row's running sum.  Such a key keeps
+                        // a weight of at most 1/4 in the output, and its bf16 rounding then counts
+                        // like that of any other key; the rescale is skipped.  Every key that
+                        // dominates a row still enters with probability exactly 1.  The sum is
+                        // the whole row's (both lane halves), so both halves decide alike.
+                        need[rb] = m_tile[rb] > m_run[rb] && fast_exp2(m_tile[rb] - m_run[rb]) * 4.f > xor32_sum(l_run[rb]);
+                    }
                     need_any = need_any || need[rb];
                 }
                 rescale_pend = __builtin_amdgcn_ballot_w64(need_any) != 0;
