@@ -172,3 +172,21 @@ def test_fp8_errors_surface():
                        torch.zeros(1, 1, 16, 32, dtype=torch.uint8, device="cuda"))
     with pytest.raises(fa.FaInvalidArgument):
         fa.forward_fp8(q8, q8.clone(), q8.clone(), descale_v=float("nan"))
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_workload_shape_fp8_sampled_rows(name):
+    """The c3 (key padding, Q/K gain 3) and c4 (N = 131072) shapes at full size with FP8 inputs,
+    checked on the workload's seed-chosen rows plus tile-boundary rows."""
+    w = W.WORKLOADS[name]
+    print(f"[case] {name} fp8: generating inputs", flush=True)
+    x = W.make_inputs(w)                      # seqlens and sampled rows in the documented order
+    q8, k8, v8, ds = W.random_qkv_fp8(w.B, w.H, w.N, w.d, w.seed, w.qk_gain)
+    mask = w.mask_kinds[0]
+    causal = bool(mask & W.MASK_CAUSAL)
+    seq = x.seqlens if (mask & W.MASK_KEY_PADDING) else None
+    rows = x.rows[:, :, :: max(1, x.rows.shape[-1] // 256)]   # about 256 rows spread over the sorted sample
+    extra = torch.tensor([0, 1, 127, 128, w.N - 1])
+    rows = torch.cat([rows, extra.expand(w.B, w.H, -1)], dim=2)
+    print(f"[case] {name} fp8: running ({rows.shape[-1]} rows per head checked)", flush=True)
+    _check(q8, k8, v8, ds, scale=x.scale, causal=causal, seqlens=seq, out_dtype=BF16, rows=rows, label=f"{name}-fp8")
