@@ -88,6 +88,15 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16(uint32_t w) {
 // scores reduced with it are finite or -inf, so NaN handling does not arise.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// max(a, b, c) as one v_maximum3_f32 (register operands only).  Written out because, given the
+// running-maximum chain m = max(m, max(a, b)), the compiler rebuilds it as a tree whose leaves
+// are two-input maxima: 24 instructions per 32 scores instead of 16.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // 16 bytes per lane from a buffer resource straight into LDS (buffer_load_dwordx4 ... lds):
 // lane i's data lands at lds + 16 i.  A device function, not a lambda, because the builtin
 // exists only for the device.
@@ -617,7 +626,7 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                             }
                         }
                         const float a0 = s_nxt[rb][fk][fr], a1 = s_nxt[rb][fk][fr + 1];
-                        mx[rb][h] = (i == 0 && e < 4) ? vmax(a0, a1) : vmax(mx[rb][h], vmax(a0, a1));
+                        mx[rb][h] = (i == 0 && e < 4) ? vmax(a0, a1) : vmax3(mx[rb][h], a0, a1);
                     }
             } else if (i == HB) {
                 bool need[RB];
