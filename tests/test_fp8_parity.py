@@ -190,3 +190,19 @@ def test_workload_shape_fp8_sampled_rows(name):
     rows = torch.cat([rows, extra.expand(w.B, w.H, -1)], dim=2)
     print(f"[case] {name} fp8: running ({rows.shape[-1]} rows per head checked)", flush=True)
     _check(q8, k8, v8, ds, scale=x.scale, causal=causal, seqlens=seq, out_dtype=BF16, rows=rows, label=f"{name}-fp8")
+
+
+def test_fa_fwd_with_fp8_dtype_equals_unit_descales():
+    """fa_fwd with in_dtype FA_DTYPE_FP8_E4M3 is fa_fwd_fp8 with every descale 1 (bitwise)."""
+    q8, k8, v8, _ = W.random_qkv_fp8(1, 2, 200, 64, seed=51)
+    q, k, v = (t.to("cuda") for t in (q8, k8, v8))
+    s = W.scale_for(64)
+    o1, l1 = fa.forward_fp8(q, k, v, scale=s, causal=True, out_dtype=F32)
+    o2 = torch.empty_like(o1)
+    l2 = torch.empty_like(l1)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = fa.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(), l2.data_ptr(), 1, 2, 200, 64, s,
+                   fa.FA_MASK_CAUSAL, None, fa.FA_DTYPE_FP8_E4M3, fa.FA_DTYPE_F32, stream)
+    assert st == fa.FA_OK
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
