@@ -295,7 +295,7 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: this benchmark measures one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the forward pass shards over (batch, head) with no "
               f"communication, so multi-GPU throughput is N x the one-GPU value by construction "
               f"and is not measured here.", file=sys.stderr)

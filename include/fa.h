@@ -50,7 +50,7 @@ typedef enum {
     FA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, unknown mask bit, padding without
                                 seqlens, scale negative or not finite, misaligned pointer,
                                 O aliasing an input, size overflow */
-    FA_ERR_UNSUPPORTED = 2,  /* valid arguments this build has no kernel for (d, dtype pair) */
+    FA_ERR_UNSUPPORTED = 2,  /* valid arguments the library has no kernel for (d, dtype pair) */
     FA_ERR_HIP = 3           /* the launch failed; fa_last_hip_error() gives the hipError_t */
 } fa_status;
 
