@@ -206,3 +206,24 @@ def test_fa_fwd_with_fp8_dtype_equals_unit_descales():
     assert st == fa.FA_OK
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_fp8_eight_wave_kernel_ragged_n():
+    """B*H*ceil(N/256) >= 1024 selects the eight-wave 256-row kernel for causal d = 128; N = 1000
+    leaves a ragged last tile (rows 768..999) and a partial diagonal.  Checked on sampled rows
+    including every tile boundary."""
+    B, H, N, d = 4, 64, 1000, 128
+    q8, k8, v8, ds = W.random_qkv_fp8(B, H, N, d, seed=61)
+    g = torch.Generator("cpu").manual_seed(62)
+    rows = torch.stack([torch.stack([torch.randperm(N, generator=g)[:24].sort().values for _ in range(H)])
+                        for _ in range(B)])
+    edge = torch.tensor([0, 1, 63, 64, 127, 128, 255, 256, 511, 512, 767, 768, 960, 998, 999])
+    rows = torch.cat([rows, edge.expand(B, H, -1)], dim=2)
+    _check(q8, k8, v8, ds, scale=W.scale_for(d), causal=True, out_dtype=BF16, rows=rows, label="fp8 eight-wave ragged")
+
+
+def test_fp8_bitwise_repeatable():
+    q8, k8, v8, ds = W.random_qkv_fp8(2, 3, 700, 64, seed=71)
+    a = _run(q8, k8, v8, ds, scale=W.scale_for(64), causal=True, out_dtype=BF16)
+    b = _run(q8, k8, v8, ds, scale=W.scale_for(64), causal=True, out_dtype=BF16)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
