@@ -10,6 +10,7 @@
 #include "fa_fwd_bf16.h"
 #include "fa_fwd_bf16_pipe.h"
 #include "fa_fwd_f32.h"
+#include "fa_fwd_ksplit.h"
 #include "fa_bwd_bf16.h"
 #include "fa_decode_bf16.h"
 
@@ -41,7 +42,15 @@ struct Launch {
 //   1  straightforward double-buffered kernel, LDS transpose reads of V
 //   2  the same with V^T gathered by 16-bit LDS reads
 //   3  the pipelined kernel with eight waves and 256-row tiles at every size (d = 128 only)
-constexpr int kNumVariants = 4;
+//   4  key split: the four waves of a workgroup share 32 query rows and divide the keys --
+//      fa_fwd's choice when the grid of variant 0 would not fill the compute units
+//   5  the four-wave pipelined kernel of variant 0 at every size (no automatic choice)
+constexpr int kNumVariants = 6;
+// fa_fwd takes the key-split kernel when variant 0 would launch at most this many workgroups
+// (an eighth of the 256 compute units or less: measured, the key split loses from 64 on) and
+// there are at least this many keys per head.
+constexpr int64_t kKeySplitMaxWgs = 32;
+constexpr int kKeySplitMinN = 256;
 // fa_fwd takes the eight-wave kernel for causal d = 128 launches with at least this many
 // 256-row tiles (over all heads); smaller grids keep two 128-row workgroups per CU.
 constexpr int64_t kWave8MinTiles = 1024;
@@ -49,12 +58,15 @@ constexpr int64_t kWave8MinTiles = 1024;
 template <int D, bool CAUSAL, bool PAD, bool OUTF32>
 Launch pick_bf16_variant(int variant) {
     switch (variant) {
-        case 0: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32>, 128, true};
+        case 0:
+        case 5: return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32>, 128, true};
         case 1: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 1>, 128, false};
         case 2: return {fa::fa_fwd_bf16_kernel<D, 64, CAUSAL, PAD, OUTF32, 0>, 128, false};
-        default:
+        case 3:
             if constexpr (D == 128) return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32, 8>, 256, true, 512};
             else return {nullptr, 0, false};
+        case 4: return {fa::fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32>, 32, false, 256};
+        default: return {nullptr, 0, false};
     }
 }
 
@@ -140,6 +152,12 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (!drop && variant == 0 && in_dtype == FA_DTYPE_BF16 && d == 128 && (mask_kind & FA_MASK_CAUSAL) &&
         static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 255) / 256) >= kWave8MinTiles)
         variant = 3;
+    // ... and grids too small to fill the chip take the key-split kernel
+    if (!drop && variant == 0 && in_dtype == FA_DTYPE_BF16 && N >= kKeySplitMinN) {
+        const int64_t n128 = (static_cast<int64_t>(N) + 127) / 128;
+        const int64_t items = (mask_kind & FA_MASK_CAUSAL) ? (n128 + 1) / 2 : n128;
+        if (static_cast<int64_t>(B) * H * items <= kKeySplitMaxWgs) variant = 4;
+    }
     Launch L;
     if (drop) {
         const bool of32 = out_dtype == FA_DTYPE_F32;

@@ -1,0 +1,270 @@
+// Key-split forward for launches too small to fill the chip (fewer work items than compute
+// units, e.g. one head of a few thousand tokens).
+//
+// The four waves of a workgroup share one 32-row query block and divide its key tiles among
+// themselves: wave w takes tiles w, w+4, w+8, ...  Each wave keeps the running maximum, sum and
+// unnormalised accumulator of the online update ("FlashAttention Interview Questions: IO
+// Complexity, Tiling, and Numerical Stability", section "How can softmax be computed across
+// tiles?") over its own keys, and at the end the four states are merged with the same
+// rescaling: m = max_w m_w, l = sum_w 2^(m_w - m) l_w, O = sum_w 2^(m_w - m) acc_w / l.  The
+// chain of tiles one wave walks is four times shorter than in the main kernel, which is what
+// bounds a launch with fewer workgroups than compute units.
+//
+// Each wave stages its own K and V tiles in its own LDS region (global -> registers -> LDS,
+// the next tile's loads in flight while the current one is computed), so the tile loop needs
+// no workgroup barrier.  The probabilities enter the value product as two bf16 terms (P_hi +
+// P_lo) with a float32 output and in masked tiles, which hold every key of a row that sees
+// fewer than one tile of keys; otherwise as one bf16 term, as in the main kernel.
+#pragma once
+
+#include <type_traits>
+
+#include "fa_fwd_bf16.h"
+
+namespace fa {
+
+template <int D, bool CAUSAL, bool PAD, bool OUT_F32>
+__global__ void __launch_bounds__(256, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
+    constexpr int NW = 4;                      // waves; each walks every NW-th key tile
+    constexpr int BM = 32;                     // query rows per workgroup (one MFMA block)
+    constexpr int BN = D == 128 ? 32 : 64;     // keys per tile
+    constexpr int KC = D / 16;                 // k-steps of the S MFMA
+    constexpr int NKB = BN / 32;               // 32-key blocks per tile
+    constexpr int NDB = D / 32;                // 32-wide output blocks
+    constexpr int PC = BN / 16;                // k-steps of the PV MFMA
+    constexpr int KSTR = D + 8;                // K row stride in LDS (elements): 16-byte pad
+    constexpr int VSTR = D + 32;               // V row stride in LDS (elements): 64-byte pad
+    constexpr int WBUF = BN * (KSTR + VSTR);   // elements of one wave's K and V tiles
+    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int LDC = BN * CPR / 64;         // chunks per lane per tensor per tile
+    constexpr int MACC = 64 * 16 * NDB;        // floats of one wave's accumulator
+    static_assert(LDC * 64 == BN * CPR, "a tile must split evenly over the 64 lanes");
+    static_assert((2 * NW * 32 + NW * MACC) * 4 <= NW * WBUF * 2, "the merge state fits in the tile buffers");
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NW * WBUF];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l32 = lane & 31;
+    const int hh = lane >> 5;
+
+    const TileCoord tc = tile_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
+    const int b = tc.bh / a.H;
+    const int N = a.N;
+    const int q0 = tc.qt * BM;
+    const int qrow = q0 + l32;                 // the query row of this lane (every wave)
+    const int64_t base = (int64_t)tc.bh * N * D;
+
+    int Lk = N;
+    if (PAD) {
+        const int s = a.seqlens[b];
+        Lk = s < 0 ? 0 : (s > N ? N : s);
+    }
+    if (Lk == 0) {  // every key masked: O = 0, LSE = -inf (written by wave 0)
+        if (wave == 0 && qrow < N) {
+            if (hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow] = kNegInf;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int d0 = 32 * db + 8 * j + 4 * hh;
+                    if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow * D + d0) = u32x2{0u, 0u};
+                }
+        }
+        return;
+    }
+
+    int kv_end = Lk;
+    if (CAUSAL) kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
+    const int n_tiles = (kv_end + BN - 1) / BN;   // >= 1: key 0 is visible to every row
+
+    bf16x8 qf[KC];   // Q^T operand: Q[qrow][16c + 8hh .. +8]
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow < N ? qrow : N - 1) * D + 8 * hh;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            qf[c] = *(const bf16x8*)(qp + 16 * c);
+            if (qrow >= N) qf[c] = bf16x8{};
+        }
+    }
+
+    uint16_t* const ks = smem + wave * WBUF;      // this wave's K tile
+    uint16_t* const vs = ks + BN * KSTR;          // and V tile
+    const uint16_t* const kg = (const uint16_t*)a.k + base;
+    const uint16_t* const vg = (const uint16_t*)a.v + base;
+    // chunk ci = lane + 64 i of a tile: row ci / CPR, column chunk ci % CPR; rows past N are
+    // read from row N - 1 (they are masked)
+    u32x4 kr[LDC], vr[LDC];
+    auto gload = [&](int tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LDC; ++i) {
+            const int ci = lane + 64 * i;
+            const int row = ci / CPR;
+            int gr = tile * BN + row;
+            gr = gr < N ? gr : N - 1;
+            kr[i] = *(const u32x4*)(kg + (int64_t)gr * D + (ci % CPR) * 8);
+            vr[i] = *(const u32x4*)(vg + (int64_t)gr * D + (ci % CPR) * 8);
+        }
+    };
+    auto swrite = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LDC; ++i) {
+            const int ci = lane + 64 * i;
+            const int row = ci / CPR;
+            *(u32x4*)(ks + row * KSTR + (ci % CPR) * 8) = kr[i];
+            *(u32x4*)(vs + row * VSTR + (ci % CPR) * 8) = vr[i];
+        }
+        // the wave's other lanes read what this lane wrote: wait for the writes to complete
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+    };
+    // V^T operand of key chunk pc and output block db by LDS transpose reads: lane (d = 32db +
+    // l32, hh) receives V[16pc + 8(e/4) + 4hh + e%4][d] for e = 0..7, the key order in which the
+    // S^T accumulator holds this lane's probabilities
+    auto vt_frag = [&](int pc, int db) __attribute__((always_inline)) -> bf16x8 {
+        const int row = 16 * pc + 4 * hh + ((l32 & 15) >> 2);
+        const int col = 32 * db + (l32 & 16) + 4 * (l32 & 3);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + row * VSTR + col)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + (row + 8) * VSTR + col)));
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+
+    float m_run = kNegInf;   // running maximum of scale*log2(e)*s over this wave's visible keys
+    float l_run = 0.f;       // this lane half's running sum of 2^(.. - m_run)
+    f32x16 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
+
+    int t = wave;
+    if (t < n_tiles) {
+        gload(t);
+        swrite();
+    }
+    for (; t < n_tiles; t += NW) {
+        const int kv0 = t * BN;
+        const int tn = t + NW;
+        if (tn < n_tiles) gload(tn);   // in flight while this tile is computed
+        f32x16 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bf16x8 kf = *(const bf16x8*)(ks + (32 * kb + l32) * KSTR + 16 * c + 8 * hh);
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+            }
+        }
+        // accumulator register r of block kb holds key kv0 + 32kb + 8(r/4) + 4hh + r%4
+        const bool need_mask = (kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kv0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const bool ok = key < Lk && (!CAUSAL || key <= qrow);
+                    s[kb][r] = ok ? s[kb][r] : kNegInf;
+                }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = xor32_max(mx);
+        const float m_tile = (mx == kNegInf) ? kNegInf : mx * a.scale_log2;
+        const float m_new = fmaxf(m_run, m_tile);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float p = fast_exp2(fmaf(s[kb][r], a.scale_log2, -m_use));
+                if (need_mask) p = s[kb][r] == kNegInf ? 0.f : p;   // exact zeros, also when scale == 0
+                s[kb][r] = p;
+                rs += p;
+            }
+        l_run = alpha * l_run + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+        // O^T += V^T P^T; key chunk pc = registers 8(pc % 2) .. +7 of block pc / 2
+        auto pv = [&](auto split_c) __attribute__((always_inline)) {
+            constexpr bool SPLIT = decltype(split_c)::value;
+#pragma unroll
+            for (int pc = 0; pc < PC; ++pc) {
+                const int kb = pc >> 1;
+                const int r0 = 8 * (pc & 1);
+                u32x4 ph, pl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    ph[e] = pack_bf16x2(s[kb][r0 + 2 * e], s[kb][r0 + 2 * e + 1]);
+                    if constexpr (SPLIT)
+                        pl[e] = pack_bf16x2(s[kb][r0 + 2 * e] - bf16_lo_to_f32(ph[e]),
+                                            s[kb][r0 + 2 * e + 1] - bf16_hi_to_f32(ph[e]));
+                }
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const bf16x8 vf = vt_frag(pc, db);
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, ph), acc[db], 0, 0, 0);
+                    if constexpr (SPLIT)
+                        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, __builtin_bit_cast(bf16x8, pl), acc[db], 0, 0, 0);
+                }
+            }
+        };
+        if (OUT_F32 || need_mask) pv(std::true_type{});
+        else pv(std::false_type{});
+        if (tn < n_tiles) swrite();   // this tile's reads have all returned (their MFMAs used them)
+    }
+
+    // merge.  LDS layout (floats): maxima [NW][32], sums [NW][32], accumulators [NW][64][16 NDB].
+    __syncthreads();   // every wave is done with its tile buffers
+    float* const ms = reinterpret_cast<float*>(smem);
+    float* const ls = ms + NW * 32;
+    float* const as = ls + NW * 32;
+    const float l_tot = xor32_sum(l_run);
+    if (hh == 0) {
+        ms[wave * 32 + l32] = m_run;
+        ls[wave * 32 + l32] = l_tot;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *(f32x4*)(as + (wave * 64 + lane) * 16 * NDB + 16 * db + 4 * j) =
+                f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
+    __syncthreads();
+    // wave w finishes accumulator registers 4w .. 4w+3 of every block: output columns
+    // 32db + 8w + 4hh + 0..3 of row qrow
+    float m = kNegInf;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) m = fmaxf(m, ms[v * 32 + l32]);
+    float sc[NW];
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const float mv = ms[v * 32 + l32];
+        sc[v] = mv == kNegInf ? 0.f : fast_exp2(mv - m);   // a wave without keys adds nothing
+        l += sc[v] * ls[v * 32 + l32];
+    }
+    if (qrow >= N) return;
+    if (wave == 0 && hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow] = (m + __log2f(l)) * kLn2;
+    const float inv_l = 1.0f / l;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int v = 0; v < NW; ++v) o += sc[v] * *(const f32x4*)(as + (v * 64 + lane) * 16 * NDB + 16 * db + 4 * wave);
+        o *= inv_l;
+        const int d0 = 32 * db + 8 * wave + 4 * hh;
+        if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow * D + d0) = o;
+        else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow * D + d0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    }
+}
+
+}  // namespace fa

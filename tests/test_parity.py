@@ -53,7 +53,7 @@ def test_sweep_bf16(N, d, mask):
                                   out_dtype=out_dtype, label=label))
 
 
-@pytest.mark.parametrize("variant", range(1, 4))
+@pytest.mark.parametrize("variant", range(1, 6))
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_variants_bf16(variant, d, mask):
@@ -65,6 +65,25 @@ def test_variants_bf16(variant, d, mask):
     seq = _seqlens(B, N, 5) if pad else None
     for out_dtype in (BF16, F32):
         label = f"variant={variant} d={d} mask={mask} out={out_dtype}"
+        print(f"[case] {label}", flush=True)
+        _report(label, check_case(q, k, v, scale=W.scale_for(d), causal=causal, seqlens=seq,
+                                  out_dtype=out_dtype, variant=variant, label=label))
+
+
+@pytest.mark.parametrize("variant", [4, 5])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 300, 1000, 2100])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_sweep_small_grid_kernels(N, d, mask, variant):
+    """Variant 4 (key split across the waves of a workgroup; fa_fwd's choice for grids smaller
+    than the chip) and variant 5 (the four-wave pipelined kernel, which fa_fwd would replace by
+    variant 4 at these sizes) over ragged sizes, every mask, both output types."""
+    causal, pad = MASKS[mask]
+    B, H = 1, 2
+    q, k, v, _ = W.random_qkv(B, H, N, d, BF16, seed=4000 + N + d)
+    seq = _seqlens(B, N, N + 5) if pad else None
+    for out_dtype in (BF16, F32):
+        label = f"variant={variant} N={N} d={d} mask={mask} out={out_dtype}"
         print(f"[case] {label}", flush=True)
         _report(label, check_case(q, k, v, scale=W.scale_for(d), causal=causal, seqlens=seq,
                                   out_dtype=out_dtype, variant=variant, label=label))
