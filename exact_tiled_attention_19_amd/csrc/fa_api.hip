@@ -42,14 +42,18 @@ struct Launch {
 //   1  straightforward double-buffered kernel, LDS transpose reads of V
 //   2  the same with V^T gathered by 16-bit LDS reads
 //   3  the pipelined kernel with eight waves and 256-row tiles at every size (d = 128 only)
-//   4  key split: the four waves of a workgroup share 32 query rows and divide the keys --
+//   4  key split: the waves of a workgroup (8 at d = 64, 4 at d = 128) share 32 query rows and
+//      divide the keys --
 //      fa_fwd's choice when the grid of variant 0 would not fill the compute units
 //   5  the four-wave pipelined kernel of variant 0 at every size (no automatic choice)
 constexpr int kNumVariants = 6;
-// fa_fwd takes the key-split kernel when variant 0 would launch at most this many workgroups
-// (an eighth of the 256 compute units or less: measured, the key split loses from 64 on) and
-// there are at least this many keys per head.
-constexpr int64_t kKeySplitMaxWgs = 32;
+// fa_fwd takes the key-split kernel when its own grid (one workgroup per 32 query rows) has at
+// most this many workgroups -- at most two (d = 64, eight waves) or a half (d = 128, four
+// waves) per compute unit of the 256 -- and there are at least this many keys per head.
+// Measured on small grids against the four-wave pipelined kernel: every case inside these
+// limits was faster (1.08-1.66x), every case outside slower (0.57-0.81x).
+constexpr int64_t kKeySplitMaxWgsD64 = 512;
+constexpr int64_t kKeySplitMaxWgsD128 = 128;
 constexpr int kKeySplitMinN = 256;
 // fa_fwd takes the eight-wave kernel for causal d = 128 launches with at least this many
 // 256-row tiles (over all heads); smaller grids keep two 128-row workgroups per CU.
@@ -65,7 +69,9 @@ Launch pick_bf16_variant(int variant) {
         case 3:
             if constexpr (D == 128) return {fa::fa_fwd_bf16_pipe_kernel<D, 64, 1, CAUSAL, PAD, OUTF32, 8>, 256, true, 512};
             else return {nullptr, 0, false};
-        case 4: return {fa::fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32>, 32, false, 256};
+        case 4:   // eight waves at d = 64; four at d = 128, where eight would not fit the registers
+            if constexpr (D == 64) return {fa::fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32, 8>, 32, false, 512};
+            else return {fa::fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32, 4>, 32, false, 256};
         default: return {nullptr, 0, false};
     }
 }
@@ -154,9 +160,8 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
         variant = 3;
     // ... and grids too small to fill the chip take the key-split kernel
     if (!drop && variant == 0 && in_dtype == FA_DTYPE_BF16 && N >= kKeySplitMinN) {
-        const int64_t n128 = (static_cast<int64_t>(N) + 127) / 128;
-        const int64_t items = (mask_kind & FA_MASK_CAUSAL) ? (n128 + 1) / 2 : n128;
-        if (static_cast<int64_t>(B) * H * items <= kKeySplitMaxWgs) variant = 4;
+        const int64_t wgs = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 31) / 32);
+        if (wgs <= (d == 64 ? kKeySplitMaxWgsD64 : kKeySplitMaxWgsD128)) variant = 4;
     }
     Launch L;
     if (drop) {

@@ -1,13 +1,13 @@
 // Key-split forward for launches too small to fill the chip (fewer work items than compute
 // units, e.g. one head of a few thousand tokens).
 //
-// The four waves of a workgroup share one 32-row query block and divide its key tiles among
-// themselves: wave w takes tiles w, w+4, w+8, ...  Each wave keeps the running maximum, sum and
+// The NW waves (eight at d = 64, four at d = 128) of a workgroup share one 32-row query block and divide its key tiles
+// among themselves: wave w takes tiles w, w+NW, w+2NW, ...  Each wave keeps the running maximum, sum and
 // unnormalised accumulator of the online update ("FlashAttention Interview Questions: IO
 // Complexity, Tiling, and Numerical Stability", section "How can softmax be computed across
 // tiles?") over its own keys, and at the end the four states are merged with the same
 // rescaling: m = max_w m_w, l = sum_w 2^(m_w - m) l_w, O = sum_w 2^(m_w - m) acc_w / l.  The
-// chain of tiles one wave walks is four times shorter than in the main kernel, which is what
+// chain of tiles one wave walks is NW times shorter than in the main kernel, which is what
 // bounds a launch with fewer workgroups than compute units.
 //
 // Each wave stages its own K and V tiles in its own LDS region (global -> registers -> LDS,
@@ -23,11 +23,14 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL, bool PAD, bool OUT_F32>
-__global__ void __launch_bounds__(256, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
-    constexpr int NW = 4;                      // waves; each walks every NW-th key tile
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <int D, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 8>
+__global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
+    // NW waves; each walks every NW-th key tile
     constexpr int BM = 32;                     // query rows per workgroup (one MFMA block)
-    constexpr int BN = D == 128 ? 32 : 64;     // keys per tile
+    constexpr int BN = (D == 128 || NW == 8) ? 32 : 64;   // keys per tile (LDS: NW tiles)
+    constexpr int RPW = 16 / NW;               // accumulator registers per block each wave finishes
     constexpr int KC = D / 16;                 // k-steps of the S MFMA
     constexpr int NKB = BN / 32;               // 32-key blocks per tile
     constexpr int NDB = D / 32;                // 32-wide output blocks
@@ -39,6 +42,7 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
     constexpr int LDC = BN * CPR / 64;         // chunks per lane per tensor per tile
     constexpr int MACC = 64 * 16 * NDB;        // floats of one wave's accumulator
     static_assert(LDC * 64 == BN * CPR, "a tile must split evenly over the 64 lanes");
+    static_assert((NW == 4 || NW == 8) && RPW * NW == 16, "each wave finishes whole register groups");
     static_assert((2 * NW * 32 + NW * MACC) * 4 <= NW * WBUF * 2, "the merge state fits in the tile buffers");
 
     __shared__ __attribute__((aligned(16))) uint16_t smem[NW * WBUF];
@@ -239,8 +243,9 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
             *(f32x4*)(as + (wave * 64 + lane) * 16 * NDB + 16 * db + 4 * j) =
                 f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
     __syncthreads();
-    // wave w finishes accumulator registers 4w .. 4w+3 of every block: output columns
-    // 32db + 8w + 4hh + 0..3 of row qrow
+    // wave w finishes accumulator registers RPW w .. RPW w + RPW - 1 of every block: register r
+    // holds output column 32db + 8(r/4) + 4hh + r%4 of row qrow, so these are RPW adjacent
+    // columns
     float m = kNegInf;
 #pragma unroll
     for (int v = 0; v < NW; ++v) m = fmaxf(m, ms[v * 32 + l32]);
@@ -255,15 +260,26 @@ __global__ void __launch_bounds__(256, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
     if (qrow >= N) return;
     if (wave == 0 && hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow] = (m + __log2f(l)) * kLn2;
     const float inv_l = 1.0f / l;
+    const int r0 = RPW * wave;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-        f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+        float o[RPW];
 #pragma unroll
-        for (int v = 0; v < NW; ++v) o += sc[v] * *(const f32x4*)(as + (v * 64 + lane) * 16 * NDB + 16 * db + 4 * wave);
-        o *= inv_l;
-        const int d0 = 32 * db + 8 * wave + 4 * hh;
-        if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow * D + d0) = o;
-        else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow * D + d0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        for (int u = 0; u < RPW; ++u) o[u] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const float* src = as + (v * 64 + lane) * 16 * NDB + 16 * db + r0;
+#pragma unroll
+            for (int u = 0; u < RPW; ++u) o[u] += sc[v] * src[u];
+        }
+        const int d0 = 32 * db + 8 * (r0 / 4) + 4 * hh + r0 % 4;
+        if constexpr (RPW == 4) {
+            if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow * D + d0) = f32x4{o[0] * inv_l, o[1] * inv_l, o[2] * inv_l, o[3] * inv_l};
+            else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow * D + d0) = u32x2{pack_bf16x2(o[0] * inv_l, o[1] * inv_l), pack_bf16x2(o[2] * inv_l, o[3] * inv_l)};
+        } else {
+            if (OUT_F32) *(f32x2*)((float*)a.o + base + (int64_t)qrow * D + d0) = f32x2{o[0] * inv_l, o[1] * inv_l};
+            else *(uint32_t*)((uint16_t*)a.o + base + (int64_t)qrow * D + d0) = pack_bf16x2(o[0] * inv_l, o[1] * inv_l);
+        }
     }
 }
 
