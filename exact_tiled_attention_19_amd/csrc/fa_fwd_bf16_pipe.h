@@ -646,7 +646,9 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                         // like that of any other key; the rescale is skipped.  Every key that
                         // dominates a row still enters with probability exactly 1.  The sum is
                         // the whole row's (both lane halves), so both halves decide alike.
-                        need[rb] = m_tile[rb] > m_run[rb] && fast_exp2(m_tile[rb] - m_run[rb]) * 4.f > xor32_sum(l_run[rb]);
+                        // With dropout a kept key's weight is further multiplied by the keep scale.
+                        const float wmul = DROP ? 4.f * a.drop_keep_scale : 4.f;
+                        need[rb] = m_tile[rb] > m_run[rb] && fast_exp2(m_tile[rb] - m_run[rb]) * wmul > xor32_sum(l_run[rb]);
                     }
                     need_any = need_any || need[rb];
                 }
