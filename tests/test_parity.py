@@ -144,3 +144,23 @@ def test_workload_full_size_sampled_rows(name):
                      out_dtype=w.out_dtypes[0], rows=rows, label=name)
     _report(name, res)
     sys.stdout.flush()
+
+
+@pytest.mark.parametrize("variant", [4, 5])
+def test_small_grid_kernels_empty_and_clamped_lengths(variant):
+    """Key padding with seqlens 0, negative (clamped to 0) and above N (clamped to N) through
+    the key-split kernel and the four-wave kernel: O = 0 and LSE = -inf for the empty batch
+    elements, never NaN; the clamped one equals the unmasked result bitwise."""
+    B, H, N, d = 3, 2, 300, 64
+    q, k, v, _ = W.random_qkv(B, H, N, d, BF16, seed=15)
+    dev = "cuda"
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    seq = torch.tensor([0, -5, 10 * N], dtype=torch.int32, device=dev)
+    for causal in (False, True):
+        for out_dtype in (BF16, F32):
+            o, lse = fa.forward(qd, kd, vd, causal=causal, seqlens=seq, out_dtype=out_dtype, variant=variant)
+            o_full, lse_full = fa.forward(qd[2:].contiguous(), kd[2:].contiguous(), vd[2:].contiguous(),
+                                          causal=causal, out_dtype=out_dtype, variant=variant)
+            torch.cuda.synchronize()
+            assert torch.all(o[:2] == 0) and torch.all(torch.isneginf(lse[:2]))
+            assert torch.equal(o[2:], o_full) and torch.equal(lse[2:], lse_full)
