@@ -50,11 +50,12 @@ constexpr int kNumVariants = 6;
 // fa_fwd takes the key-split kernel when its own grid (one workgroup per 32 query rows) has at
 // most this many workgroups -- at most two (d = 64, eight waves) or a half (d = 128, four
 // waves) per compute unit of the 256 -- and there are at least this many keys per head.
-// Measured on small grids against the four-wave pipelined kernel: every case inside these
-// limits was faster (1.08-1.66x), every case outside slower (0.57-0.81x).
+// Measured on small grids against the four-wave pipelined kernel: inside these limits the key
+// split was faster or level (0.98-2.1x), outside them slower (0.57-0.81x).  Below 512 keys a
+// wave has at most one tile and splitting only adds the merge (N = 256: 0.68x).
 constexpr int64_t kKeySplitMaxWgsD64 = 512;
 constexpr int64_t kKeySplitMaxWgsD128 = 128;
-constexpr int kKeySplitMinN = 256;
+constexpr int kKeySplitMinN = 512;
 // fa_fwd takes the eight-wave kernel for causal d = 128 launches with at least this many
 // 256-row tiles (over all heads); smaller grids keep two 128-row workgroups per CU.
 constexpr int64_t kWave8MinTiles = 1024;
