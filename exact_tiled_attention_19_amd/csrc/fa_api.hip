@@ -172,9 +172,12 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     } else if (f8) {
         const bool wide = d == 128 && (mask_kind & FA_MASK_CAUSAL) &&
                           static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 255) / 256) >= kWave8MinTiles;
+        // small grids take the key split, by the same rule as bf16 inputs
+        const int64_t ks_wgs = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 31) / 32);
+        const bool small = N >= kKeySplitMinN && ks_wgs <= (d == 64 ? kKeySplitMaxWgsD64 : kKeySplitMaxWgsD128);
         int bm = 0, threads = 0;
-        const Kernel kern = fa::pick_fp8_kernel(d, mask_kind, out_dtype == FA_DTYPE_F32, wide, &bm, &threads);
-        L = {kern, bm, true, threads};
+        const Kernel kern = fa::pick_fp8_kernel(d, mask_kind, out_dtype == FA_DTYPE_F32, wide && !small, small, &bm, &threads);
+        L = {kern, bm, !small, threads};   // the key split runs single 32-row blocks, never tile pairs
     } else if (in_dtype == FA_DTYPE_BF16) {
         const bool of32 = out_dtype == FA_DTYPE_F32;
         if (d == 64) L = of32 ? pick_bf16_mask<64, true>(mask_kind, variant) : pick_bf16_mask<64, false>(mask_kind, variant);

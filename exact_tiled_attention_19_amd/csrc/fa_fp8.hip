@@ -3,12 +3,19 @@
 #include <hip/hip_runtime.h>
 
 #include "fa_fwd_bf16_pipe.h"
+#include "fa_fwd_ksplit.h"
 
 namespace fa {
 namespace {
 
 template <int D, bool CAUSAL, bool PAD, bool OUTF32>
-FwdKernelFn fp8_nw(bool wide, int* bm, int* threads) {
+FwdKernelFn fp8_nw(bool wide, bool small, int* bm, int* threads) {
+    if (small) {   // key split: eight waves at d = 64, four at d = 128
+        constexpr int NW = D == 64 ? 8 : 4;
+        *bm = 32;
+        *threads = 64 * NW;
+        return fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32, NW, true>;
+    }
     if constexpr (D == 128 && CAUSAL) {
         if (wide) {   // one eight-wave, 256-row workgroup per CU (long causal d = 128 heads)
             *bm = 256;
@@ -22,20 +29,22 @@ FwdKernelFn fp8_nw(bool wide, int* bm, int* threads) {
 }
 
 template <int D, bool OUTF32>
-FwdKernelFn fp8_mask(int mask, bool wide, int* bm, int* threads) {
+FwdKernelFn fp8_mask(int mask, bool wide, bool small, int* bm, int* threads) {
     switch (mask) {
-        case 0: return fp8_nw<D, false, false, OUTF32>(wide, bm, threads);
-        case 1: return fp8_nw<D, true, false, OUTF32>(wide, bm, threads);
-        case 2: return fp8_nw<D, false, true, OUTF32>(wide, bm, threads);
-        default: return fp8_nw<D, true, true, OUTF32>(wide, bm, threads);
+        case 0: return fp8_nw<D, false, false, OUTF32>(wide, small, bm, threads);
+        case 1: return fp8_nw<D, true, false, OUTF32>(wide, small, bm, threads);
+        case 2: return fp8_nw<D, false, true, OUTF32>(wide, small, bm, threads);
+        default: return fp8_nw<D, true, true, OUTF32>(wide, small, bm, threads);
     }
 }
 
 }  // namespace
 
-FwdKernelFn pick_fp8_kernel(int d, int mask, bool out_f32, bool wide, int* bm, int* threads) {
-    if (d == 64) return out_f32 ? fp8_mask<64, true>(mask, false, bm, threads) : fp8_mask<64, false>(mask, false, bm, threads);
-    if (d == 128) return out_f32 ? fp8_mask<128, true>(mask, wide, bm, threads) : fp8_mask<128, false>(mask, wide, bm, threads);
+FwdKernelFn pick_fp8_kernel(int d, int mask, bool out_f32, bool wide, bool small, int* bm, int* threads) {
+    if (d == 64)
+        return out_f32 ? fp8_mask<64, true>(mask, false, small, bm, threads) : fp8_mask<64, false>(mask, false, small, bm, threads);
+    if (d == 128)
+        return out_f32 ? fp8_mask<128, true>(mask, wide, small, bm, threads) : fp8_mask<128, false>(mask, wide, small, bm, threads);
     return nullptr;
 }
 

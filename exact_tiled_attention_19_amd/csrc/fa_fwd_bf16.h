@@ -72,10 +72,11 @@ struct FwdArgs {
 using FwdKernelFn = void (*)(FwdArgs);
 
 // The forward kernel for FP8 E4M3 inputs (fa_fp8.hip) for head width d, mask bits `mask` and
-// output type; `wide` asks for the eight-wave 256-row workgroup where one exists.  Sets the
-// query rows per tile (*bm) and threads per workgroup; nullptr when d has no kernel.
-__attribute__((visibility("hidden"))) FwdKernelFn pick_fp8_kernel(int d, int mask, bool out_f32, bool wide, int* bm,
-                                                                  int* threads);
+// output type; `wide` asks for the eight-wave 256-row workgroup where one exists, `small` for
+// the key-split kernel of small grids.  Sets the query rows per tile (*bm) and threads per
+// workgroup; nullptr when d has no kernel.
+__attribute__((visibility("hidden"))) FwdKernelFn pick_fp8_kernel(int d, int mask, bool out_f32, bool wide, bool small,
+                                                                  int* bm, int* threads);
 
 // Where the rows of one head of one sequence live, and which keys its queries may see.
 struct SeqGeom {

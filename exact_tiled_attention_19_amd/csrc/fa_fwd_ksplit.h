@@ -15,37 +15,45 @@
 // no workgroup barrier.  The probabilities enter the value product as two bf16 terms (P_hi +
 // P_lo) with a float32 output and in masked tiles, which hold every key of a row that sees
 // fewer than one tile of keys; otherwise as one bf16 term, as in the main kernel.
+//
+// F8: FP8 E4M3 inputs with per-tensor descales, as in the pipelined FP8 kernel: S on the 8-bit
+// MFMA with Q and K fragments taking the same byte -> dimension assignment, V widened to bf16
+// (exactly) as it is written to LDS, the value descale applied to the output.
 #pragma once
 
 #include <type_traits>
 
-#include "fa_fwd_bf16.h"
+#include "fa_fwd_bf16_pipe.h"
 
 namespace fa {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-template <int D, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 8>
+template <int D, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 8, bool F8 = false>
 __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
     // NW waves; each walks every NW-th key tile
     constexpr int BM = 32;                     // query rows per workgroup (one MFMA block)
     constexpr int BN = (D == 128 || NW == 8) ? 32 : 64;   // keys per tile (LDS: NW tiles)
     constexpr int RPW = 16 / NW;               // accumulator registers per block each wave finishes
-    constexpr int KC = D / 16;                 // k-steps of the S MFMA
+    constexpr int ESZ = F8 ? 1 : 2;            // bytes per input element
+    constexpr int KC = F8 ? D / 64 : D / 16;   // k-steps of the S MFMA
     constexpr int NKB = BN / 32;               // 32-key blocks per tile
     constexpr int NDB = D / 32;                // 32-wide output blocks
     constexpr int PC = BN / 16;                // k-steps of the PV MFMA
-    constexpr int KSTR = D + 8;                // K row stride in LDS (elements): 16-byte pad
-    constexpr int VSTR = D + 32;               // V row stride in LDS (elements): 64-byte pad
-    constexpr int WBUF = BN * (KSTR + VSTR);   // elements of one wave's K and V tiles
-    constexpr int CPR = D / 8;                 // 16-byte chunks per row
+    constexpr int KROWB = D * ESZ + 16;        // K row stride in LDS (bytes): 16-byte pad
+    constexpr int VSTR = D + 32;               // V row stride in LDS (bf16 elements): 64-byte pad
+    constexpr int WBUFB = BN * KROWB + BN * VSTR * 2;   // bytes of one wave's K and V tiles
+    constexpr int CPR = D * ESZ / 16;          // 16-byte input chunks per row
     constexpr int LDC = BN * CPR / 64;         // chunks per lane per tensor per tile
     constexpr int MACC = 64 * 16 * NDB;        // floats of one wave's accumulator
+    constexpr int MERGEB = (2 * NW * 32 + NW * MACC) * 4;   // bytes of the merge state
+    constexpr int SMEMB = NW * WBUFB > MERGEB ? NW * WBUFB : MERGEB;
+    using KFrag = std::conditional_t<F8, i32x8, bf16x8>;
     static_assert(LDC * 64 == BN * CPR, "a tile must split evenly over the 64 lanes");
     static_assert((NW == 4 || NW == 8) && RPW * NW == 16, "each wave finishes whole register groups");
-    static_assert((2 * NW * 32 + NW * MACC) * 4 <= NW * WBUF * 2, "the merge state fits in the tile buffers");
+    static_assert(KROWB % 16 == 0 && WBUFB % 16 == 0, "16-byte LDS accesses stay aligned");
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem[NW * WBUF];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEMB];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -84,20 +92,26 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     if (CAUSAL) kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
     const int n_tiles = (kv_end + BN - 1) / BN;   // >= 1: key 0 is visible to every row
 
-    bf16x8 qf[KC];   // Q^T operand: Q[qrow][16c + 8hh .. +8]
+    // Q^T operand: bf16 Q[qrow][16c + 8hh .. +8]; 8-bit: bytes 64c + 32hh .. +32 of the row (the
+    // K fragments below take the same bytes of their rows)
+    KFrag qf[KC];
     {
-        const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow < N ? qrow : N - 1) * D + 8 * hh;
+        const unsigned char* qp = (const unsigned char*)a.q + (base + (int64_t)(qrow < N ? qrow : N - 1) * D) * ESZ;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
-            qf[c] = *(const bf16x8*)(qp + 16 * c);
-            if (qrow >= N) qf[c] = bf16x8{};
+            if constexpr (F8)
+                qf[c] = __builtin_bit_cast(i32x8, u32x8_of(*(const u32x4*)(qp + 64 * c + 32 * hh),
+                                                           *(const u32x4*)(qp + 64 * c + 32 * hh + 16)));
+            else
+                qf[c] = *(const bf16x8*)(qp + 32 * c + 16 * hh);
+            if (qrow >= N) qf[c] = KFrag{};
         }
     }
 
-    uint16_t* const ks = smem + wave * WBUF;      // this wave's K tile
-    uint16_t* const vs = ks + BN * KSTR;          // and V tile
-    const uint16_t* const kg = (const uint16_t*)a.k + base;
-    const uint16_t* const vg = (const uint16_t*)a.v + base;
+    unsigned char* const ks = smem + wave * WBUFB;              // this wave's K tile (bytes)
+    uint16_t* const vs = (uint16_t*)(ks + BN * KROWB);          // and V tile (bf16)
+    const unsigned char* const kg = (const unsigned char*)a.k + base * ESZ;
+    const unsigned char* const vg = (const unsigned char*)a.v + base * ESZ;
     // chunk ci = lane + 64 i of a tile: row ci / CPR, column chunk ci % CPR; rows past N are
     // read from row N - 1 (they are masked)
     u32x4 kr[LDC], vr[LDC];
@@ -108,8 +122,8 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
             const int row = ci / CPR;
             int gr = tile * BN + row;
             gr = gr < N ? gr : N - 1;
-            kr[i] = *(const u32x4*)(kg + (int64_t)gr * D + (ci % CPR) * 8);
-            vr[i] = *(const u32x4*)(vg + (int64_t)gr * D + (ci % CPR) * 8);
+            kr[i] = *(const u32x4*)(kg + (int64_t)gr * D * ESZ + (ci % CPR) * 16);
+            vr[i] = *(const u32x4*)(vg + (int64_t)gr * D * ESZ + (ci % CPR) * 16);
         }
     };
     auto swrite = [&]() __attribute__((always_inline)) {
@@ -117,8 +131,15 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
         for (int i = 0; i < LDC; ++i) {
             const int ci = lane + 64 * i;
             const int row = ci / CPR;
-            *(u32x4*)(ks + row * KSTR + (ci % CPR) * 8) = kr[i];
-            *(u32x4*)(vs + row * VSTR + (ci % CPR) * 8) = vr[i];
+            *(u32x4*)(ks + row * KROWB + (ci % CPR) * 16) = kr[i];
+            if constexpr (F8) {   // 16 codes = dimensions 16 (ci % CPR) .. +16, widened to bf16
+                const u32x2 w0 = e4m3x4_to_bf16(vr[i][0]), w1 = e4m3x4_to_bf16(vr[i][1]);
+                const u32x2 w2 = e4m3x4_to_bf16(vr[i][2]), w3 = e4m3x4_to_bf16(vr[i][3]);
+                *(u32x4*)(vs + row * VSTR + (ci % CPR) * 16) = u32x4{w0[0], w0[1], w1[0], w1[1]};
+                *(u32x4*)(vs + row * VSTR + (ci % CPR) * 16 + 8) = u32x4{w2[0], w2[1], w3[0], w3[1]};
+            } else {
+                *(u32x4*)(vs + row * VSTR + (ci % CPR) * 8) = vr[i];
+            }
         }
         // the wave's other lanes read what this lane wrote: wait for the writes to complete
         __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -157,8 +178,14 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
             s[kb] = f32x16{};
 #pragma unroll
             for (int c = 0; c < KC; ++c) {
-                const bf16x8 kf = *(const bf16x8*)(ks + (32 * kb + l32) * KSTR + 16 * c + 8 * hh);
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[c], s[kb], 0, 0, 0);
+                const unsigned char* kp = ks + (32 * kb + l32) * KROWB;
+                KFrag kf;
+                if constexpr (F8)
+                    kf = __builtin_bit_cast(i32x8, u32x8_of(*(const u32x4*)(kp + 64 * c + 32 * hh),
+                                                            *(const u32x4*)(kp + 64 * c + 32 * hh + 16)));
+                else
+                    kf = *(const bf16x8*)(kp + 32 * c + 16 * hh);
+                s[kb] = mfma_s(kf, qf[c], s[kb]);
             }
         }
         // accumulator register r of block kb holds key kv0 + 32kb + 8(r/4) + 4hh + r%4
@@ -259,7 +286,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     }
     if (qrow >= N) return;
     if (wave == 0 && hh == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow] = (m + __log2f(l)) * kLn2;
-    const float inv_l = 1.0f / l;
+    const float inv_l = (F8 ? a.v_descale : 1.0f) / l;   // 8-bit inputs: V's descale
     const int r0 = RPW * wave;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {

@@ -227,3 +227,22 @@ def test_fp8_bitwise_repeatable():
     a = _run(q8, k8, v8, ds, scale=W.scale_for(64), causal=True, out_dtype=BF16)
     b = _run(q8, k8, v8, ds, scale=W.scale_for(64), causal=True, out_dtype=BF16)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [512, 777, 2100])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_sweep_fp8_key_split(N, d, mask):
+    """Grids small enough for the key split (B*H*ceil(N/32) within its limits, N >= 512): the
+    8-bit key-split kernel, every mask, both output types, ragged sizes."""
+    causal, pad = MASKS[mask]
+    B, H = 1, 2
+    q8, k8, v8, ds = W.random_qkv_fp8(B, H, N, d, seed=5000 + N + d)
+    seq = None
+    if pad:
+        g = torch.Generator("cpu").manual_seed(N + 13)
+        seq = torch.randint(0, N + 1, (B,), generator=g, dtype=torch.int32)
+    for out_dtype in (BF16, F32):
+        label = f"key split N={N} d={d} mask={mask} out={out_dtype}"
+        print(f"[case] {label}", flush=True)
+        _check(q8, k8, v8, ds, scale=W.scale_for(d), causal=causal, seqlens=seq, out_dtype=out_dtype, label=label)
