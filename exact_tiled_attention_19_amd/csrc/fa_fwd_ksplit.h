@@ -1,14 +1,15 @@
 // Key-split forward for launches too small to fill the chip (fewer work items than compute
 // units, e.g. one head of a few thousand tokens).
 //
-// The NW waves (eight at d = 64, four at d = 128) of a workgroup share one 32-row query block and divide its key tiles
-// among themselves: wave w takes tiles w, w+NW, w+2NW, ...  Each wave keeps the running maximum, sum and
-// unnormalised accumulator of the online update ("FlashAttention Interview Questions: IO
-// Complexity, Tiling, and Numerical Stability", section "How can softmax be computed across
-// tiles?") over its own keys, and at the end the four states are merged with the same
-// rescaling: m = max_w m_w, l = sum_w 2^(m_w - m) l_w, O = sum_w 2^(m_w - m) acc_w / l.  The
-// chain of tiles one wave walks is NW times shorter than in the main kernel, which is what
-// bounds a launch with fewer workgroups than compute units.
+// The NW waves of a workgroup (eight at d = 64, four at d = 128) share one 32-row query block
+// and divide its key tiles among themselves: wave w takes tiles w, w+NW, w+2NW, ...  Each wave
+// keeps the running maximum, sum and unnormalised accumulator of the online update
+// ("FlashAttention Interview Questions: IO Complexity, Tiling, and Numerical Stability",
+// section "How can softmax be computed across tiles?") over its own keys, and at the end the NW
+// states are merged with the same rescaling: m = max_w m_w, l = sum_w 2^(m_w - m) l_w,
+// O = sum_w 2^(m_w - m) acc_w / l.  The chain of tiles one wave walks is about NW times
+// shorter than in the main kernel, and that chain is what bounds a launch with fewer
+// workgroups than compute units.
 //
 // Each wave stages its own K and V tiles in its own LDS region (global -> registers -> LDS,
 // the next tile's loads in flight while the current one is computed), so the tile loop needs
