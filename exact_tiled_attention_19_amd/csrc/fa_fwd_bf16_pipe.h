@@ -18,12 +18,15 @@
 //     consumed inside one iteration, so only the scores are double-buffered.  The iteration is
 //     written as a fixed sequence of slots, one MFMA with its LDS read and a slice of vector
 //     work each, kept in that order by sched_barrier.
-//   * Shift policy.  With a bf16 output the shift is the exact running row maximum, so the
-//     largest probability of every row is exactly 1 and carries no bf16 rounding; the
-//     accumulator is rescaled (per row, applied wave-wide) whenever some row's maximum rises.
-//     With a float32 output (P = P_hi + P_lo, two bf16 products) the shift is raised only when
-//     a row's tile maximum exceeds it by more than 8 (log2 units), which skips most rescales.
-//     Numerator and denominator share every shift, so the result is unchanged.
+//   * Shift policy.  With a bf16 output the shift follows the running row maximum, so the
+//     key that dominates a row enters with probability exactly 1 and carries no bf16
+//     rounding; a rise is left unapplied only while the new largest probability is at most a
+//     quarter of the row's running sum and the rise is at most 8 (log2 units).  With a float32
+//     output (P = P_hi + P_lo, two bf16 products) the shift is raised only when a row's tile
+//     maximum exceeds it by more than 8, which skips most rescales.  Either way every
+//     probability stays at most 2^8, and numerator and denominator share every shift, so the
+//     result is unchanged.  The accumulator is rescaled (per row, applied wave-wide) whenever
+//     some row's shift moves.
 //   * Probability precision.  The value product takes P as one bf16 term (relative rounding
 //     up to 2^-9) except where that error is not averaged away: a float32 output always uses
 //     P_hi + P_lo, and with a bf16 output so do the masked tiles of a wave with a row that sees
@@ -144,6 +147,9 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     // probability is then exactly 1 and carries no rounding); with the two-term split used for
     // a float32 output a shift lagging by up to 8 costs nothing.
     constexpr float kTau = PRECISE ? 8.0f : 0.0f;
+    // Largest rise of the row maximum (log2 units) that the bf16-output rule below may leave
+    // unapplied; the float32-output threshold kTau bounds the probabilities by the same 2^8.
+    constexpr float kSkipCap = 8.0f;
     static_assert(LPW >= 1 && LPW * NW * 1024 == KTILEB, "tile must split into 1 KiB pieces");
     static_assert(!F8 || (!DROP && !VL && RB == 1), "8-bit inputs: fixed-length heads without dropout");
     static_assert(!DROP || (RB == 1 && BN == 64 && !VL), "dropout words are laid out for one 32-row block");
@@ -647,8 +653,15 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                         // dominates a row still enters with probability exactly 1.  The sum is
                         // the whole row's (both lane halves), so both halves decide alike.
                         // With dropout a kept key's weight is further multiplied by the keep scale.
+                        // The skip is capped: a rise of more than kSkipCap always moves the
+                        // shift, so every probability stays at most 2^kSkipCap and the sum at
+                        // most that times the key count.  Without the cap, logits that climb a
+                        // little per tile (each rise small against the grown sum) never move
+                        // the shift, and the sum overflows float32 once the climb passes
+                        // about 88 nats (2^128).
                         const float wmul = DROP ? 4.f * a.drop_keep_scale : 4.f;
-                        need[rb] = m_tile[rb] > m_run[rb] && fast_exp2(m_tile[rb] - m_run[rb]) * wmul > xor32_sum(l_run[rb]);
+                        const float rise = m_tile[rb] - m_run[rb];
+                        need[rb] = rise > 0.f && (rise > kSkipCap || fast_exp2(rise) * wmul > xor32_sum(l_run[rb]));
                     }
                     need_any = need_any || need[rb];
                 }

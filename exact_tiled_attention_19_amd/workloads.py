@@ -58,10 +58,9 @@ WORKLOADS = {
                    (MASK_NONE, MASK_CAUSAL), seed=1,
                    description="memory-budget example N=4096 d=64; non-causal and causal; bf16 and fp32 out"),
     "c2": Workload("c2", 4, 16, 8192, 128, torch.bfloat16, (torch.bfloat16,), (MASK_CAUSAL,), seed=2,
-                   sample_rows=256, description="batched causal, the throughput/roofline workload"),
+                   description="batched causal, the throughput/roofline workload"),
     "c3": Workload("c3", 2, 32, 16384, 64, torch.bfloat16, (torch.bfloat16,), (MASK_KEY_PADDING,), seed=3,
-                   qk_gain=3.0, sample_rows=256,
-                   description="key padding, Q and K x3 so logit std ~ 9"),
+                   qk_gain=3.0, description="key padding, Q and K x3 so logit std ~ 9"),
     "c4": Workload("c4", 1, 8, 131072, 128, torch.bfloat16, (torch.bfloat16,), (MASK_CAUSAL,), seed=4,
                    sample_rows=1024, description="long-context causal, 1024 sampled rows per head"),
 }
@@ -100,6 +99,23 @@ def random_qkv(B: int, H: int, N: int, d: int, dtype: torch.dtype, seed: int,
         q.mul_(qk_gain)
         k.mul_(qk_gain)
     return q.to(dtype), k.to(dtype), v.to(dtype), g
+
+
+def ramp_qkv(B: int, H: int, N: int, d: int, span: float, dtype: torch.dtype, seed: int):
+    """Logits that climb steadily along the keys: q_i = a u + 0.05 n_i, k_j = a (j / N) u + 0.05 n_j
+    (u the all-ones vector, n standard normals), V standard normal, cast to ``dtype``; CPU tensors.
+
+    a = sqrt(span / sqrt(d)), so with the scale 1/sqrt(d) the score of key j for any query is about
+    span * j / N: each key tile raises the row maximum a little and the whole row climbs by about
+    ``span`` (natural-log units).  Draw order: the query noise, the key noise, V.
+    """
+    g = torch.Generator("cpu").manual_seed(seed)
+    a = math.sqrt(span / math.sqrt(d))
+    ramp = torch.arange(N, dtype=torch.float32) / N
+    q = a + 0.05 * torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    k = a * ramp[:, None] + 0.05 * torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, N, d, generator=g, dtype=torch.float32)
+    return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
 def to_e4m3(x: torch.Tensor):

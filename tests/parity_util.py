@@ -10,7 +10,11 @@ Tolerances (bf16 operands, float32 accumulation):
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
+import threadpoolctl
 import torch
 
 import exact_tiled_attention_19_amd as fa
@@ -40,6 +44,33 @@ def gpu_forward(q, k, v, *, scale, causal, seqlens, out_dtype, variant=0, device
                         variant=variant)
     torch.cuda.synchronize()
     return o.cpu(), lse.cpu()
+
+
+def oracle_threads() -> int:
+    """Host threads for oracle work: the CPUs this process may use, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def attention_ref_heads(q, k, v, scale, causal=False, seqlens=None, rows=None):
+    """``oracle.attention_ref`` called once per (batch, head) on a thread pool, each call with a
+    single-threaded BLAS; the results are stacked back to [B, H, R, d] and [B, H, R].  The
+    oracle itself is unchanged: numpy releases the interpreter lock inside its array work, so the
+    heads run side by side (full-size workloads would otherwise take minutes)."""
+    B, H = q.shape[:2]
+    r = None if rows is None else np.asarray(rows.cpu().numpy() if hasattr(rows, "numpy") else rows)
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        rr = None if r is None else (r if r.ndim == 1 else r[b:b + 1, h:h + 1])
+        sl = None if seqlens is None else [int(seqlens[b])]
+        return oracle.attention_ref(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], v[b:b + 1, h:h + 1], scale,
+                                    causal=causal, seqlens=sl, rows=rr)
+
+    with threadpoolctl.threadpool_limits(1), ThreadPoolExecutor(oracle_threads()) as ex:
+        parts = list(ex.map(one, range(B * H)))
+    O = np.stack([p[0][0, 0] for p in parts]).reshape(B, H, *parts[0][0].shape[2:])
+    L = np.stack([p[1][0, 0] for p in parts]).reshape(B, H, -1)
+    return O, L
 
 
 def select_rows(x: torch.Tensor, rows) -> np.ndarray:
@@ -86,7 +117,9 @@ def check_case(q, k, v, *, scale, causal=False, seqlens=None, out_dtype=torch.bf
                variant=0, label=""):
     o, lse = gpu_forward(q, k, v, scale=scale, causal=causal, seqlens=seqlens, out_dtype=out_dtype,
                          variant=variant)
-    O_ref, LSE_ref = oracle.attention_ref(q, k, v, scale, causal=causal,
-                                          seqlens=None if seqlens is None else seqlens.tolist(),
-                                          rows=rows)
+    sl = None if seqlens is None else seqlens.tolist()
+    if q.shape[0] * q.shape[1] > 1 and q.shape[2] >= 1024:
+        O_ref, LSE_ref = attention_ref_heads(q, k, v, scale, causal=causal, seqlens=sl, rows=rows)
+    else:
+        O_ref, LSE_ref = oracle.attention_ref(q, k, v, scale, causal=causal, seqlens=sl, rows=rows)
     return compare(o, lse, O_ref, LSE_ref, out_dtype, rows=rows, label=label)
