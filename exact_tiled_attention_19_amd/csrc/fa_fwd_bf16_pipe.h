@@ -398,6 +398,18 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         for (int db = 0; db < NDB; ++db) acc[rb][db] = f32x16{};
     }
     bool rescale_pend = false;
+    // Heavy-tile test (bf16 output, one-term probabilities), for the tile whose scores were last
+    // prepared: 1 when that tile's row maximum became the shift and lies in this lane half (its
+    // key's probability is then 1 up to a float32 rounding, exact in bf16), else 0.
+    float one_pend[RB];
+    // Whether this lane half of the current tile is heavy (its P_lo is used; other lanes add
+    // exactly zero).
+    bool hv_lane[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        one_pend[rb] = 0.f;
+        hv_lane[rb] = false;
+    }
 
     // Multiplier of the masked steps' fma: scale*log2(e), or the smallest normal float when the
     // scale is 0 (then every visible t is within 1e-30 of 0, as it should be, and -inf * c
@@ -430,10 +442,12 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = (kb == 0 ? 1 : 0); r < 16; ++r) mx = vmax(mx, s[rb][kb][r]);
+            const float hmx = mx;
             mx = xor32_max(mx);
             m_tile[rb] = (mx == kNegInf) ? kNegInf : mx * a.scale_log2;
             need[rb] = m_tile[rb] > m_run[rb] + kTau;     // per row: the update depends on
             need_any = need_any || need[rb];              // this row's scores only
+            one_pend[rb] = (need[rb] && hmx == mx) ? 1.f : 0.f;
         }
         const bool any = __builtin_amdgcn_ballot_w64(need_any) != 0;   // wave-uniform
 #pragma unroll
@@ -523,6 +537,43 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
         const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * ROWB)));
         return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     };
+    // The heavy tile's second term (see fast_body): P_lo = p - bf16(p), from the probabilities
+    // that phase A left in the score registers of parity PAR, times that tile's V (buffer PAR,
+    // refilled only after the iteration's closing barrier), for the lane halves found heavy; the
+    // others contribute exactly 0.
+    auto heavy_fix = [&](auto par_c) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par_c)::value;
+        f32x16 (&sp)[RB][NKB] = PAR == 0 ? sA : sB;
+        constexpr int VB_T = PAR == 0 ? VB0 : VB1;
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) {
+            u32x4 lo[RB];   // this k-step's P_lo only (the register budget decides occupancy)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int f = 8 * pc + 2 * w, fk = f / 16, fr = f % 16;
+                    const float h0 = bf16_lo_to_f32(ph[rb][pc][w]), h1 = bf16_hi_to_f32(ph[rb][pc][w]);
+                    float r0 = sp[rb][fk][fr] - h0, r1 = sp[rb][fk][fr + 1] - h1;
+                    if constexpr (DROP) {   // a dropped key entered as 0: its residual is 0 too
+                        r0 = h0 == 0.f ? 0.f : r0;
+                        r1 = h1 == 0.f ? 0.f : r1;
+                    }
+                    r0 = hv_lane[rb] ? r0 : 0.f;
+                    r1 = hv_lane[rb] ? r1 : 0.f;
+                    lo[rb][w] = pack_bf16x2(r0, r1);
+                }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x8 v2 = vfrag(VB_T, pc * NDB + db);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v2, __builtin_bit_cast(bf16x8, lo[rb]),
+                                                                          acc[rb][db], 0, 0, 0);
+            }
+        }
+    };
+
     auto fast_body = [&](auto par_c, auto masked_c, auto split_c, int j) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par_c)::value;
         constexpr bool MASKED = decltype(masked_c)::value;
@@ -597,8 +648,56 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
             kf1 = kf2;
             __builtin_amdgcn_sched_barrier(0);
         }
+        // Heavy tile (bf16 output, one-term probabilities).  A probability rounded to bf16 errs by
+        // up to 2^-8 of itself, which stays far inside the output's bound for keys of small
+        // weight, but a key that ends with a large share of its row (two near-equal dominant
+        // keys, say) can move O by a few 1e-3: too much where |O| is in [2, 4) and the output's
+        // own rounding already takes up to 7.8e-3 of the 1e-2 bound.  So a lane half whose keys
+        // of tile j may end with more than a quarter of the row's weight -- a probability above
+        // l/4, with l the row sum including tile j, which can only grow -- also gets P_lo =
+        // p - bf16(p), in an extra value product after phase B (run when any lane needs it; the
+        // other lanes add exactly 0, so every row's result depends on its own scores only).
+        // The bound on one key's probability is the half's share of the tile's sum, less the
+        // exact 1 of the shift's own maximum when it lies in this half, and at most 1 (the shift
+        // is at or above every score of the tile, or else, by the rescale rule, every
+        // probability of the tile is at most l/4 already).  The test and the extra product
+        // (heavy_fix) run between the phases, while the probabilities are still in registers.
+        constexpr bool DYN = !SPLIT;
+        float rsum[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) l_run[rb] += rs[rb][0] + rs[rb][1];
+        for (int rb = 0; rb < RB; ++rb) {
+            rsum[rb] = rs[rb][0] + rs[rb][1];
+            l_run[rb] += rsum[rb];
+        }
+        float l_all[RB];   // the whole row's running sum (both lane halves), tiles <= j
+        if constexpr (DYN) {
+            const float wmul_h = DROP ? 4.f * a.drop_keep_scale : 4.f;   // kept keys weigh 1/(1-p) more
+            bool small_any = false;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                l_all[rb] = xor32_sum(l_run[rb]);
+                small_any = small_any || l_all[rb] < wmul_h;   // the test can only pass when l < 4
+            }
+            // Phase A's results feed phase B; without these (empty) uses the compiler would sink
+            // their computation past the branches below, away from the MFMAs of phase A.
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+                for (int pc = 0; pc < PC; ++pc) asm volatile("" : "+v"(ph[rb][pc]));
+                asm volatile("" : "+v"(l_run[rb]), "+v"(l_all[rb]));
+            }
+            bool heavy = false;
+            if (__builtin_amdgcn_ballot_w64(small_any) != 0) {
+                bool hv_any = false;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    hv_lane[rb] = fminf(rsum[rb] - one_pend[rb], 1.f) * wmul_h > l_all[rb];
+                    hv_any = hv_any || hv_lane[rb];
+                }
+                heavy = __builtin_amdgcn_ballot_w64(hv_any) != 0;
+            }
+            if (heavy) heavy_fix(par_c);
+        }
         // phase B
         float mx[RB][2];
         bf16x8 vf = vfrag(VB_THIS, 0);
@@ -638,9 +737,14 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                 bool need[RB];
                 bool need_any = false;
                 float m_tile[RB];
+                if constexpr (!PRECISE && !DYN) {
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb) l_all[rb] = xor32_sum(l_run[rb]);
+                }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
-                    const float m = xor32_max(vmax(mx[rb][0], mx[rb][1]));
+                    const float hmx = vmax(mx[rb][0], mx[rb][1]);
+                    const float m = xor32_max(hmx);
                     m_tile[rb] = m * a.scale_log2;
                     if constexpr (PRECISE) {
                         need[rb] = m_tile[rb] > m_run[rb] + kTau;
@@ -661,7 +765,9 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                         // about 88 nats (2^128).
                         const float wmul = DROP ? 4.f * a.drop_keep_scale : 4.f;
                         const float rise = m_tile[rb] - m_run[rb];
-                        need[rb] = rise > 0.f && (rise > kSkipCap || fast_exp2(rise) * wmul > xor32_sum(l_run[rb]));
+                        need[rb] = rise > 0.f && (rise > kSkipCap || fast_exp2(rise) * wmul > l_all[rb]);
+                        // for tile j+1's heavy test: its maximum is the shift and lies in this half
+                        one_pend[rb] = (need[rb] && hmx == m) ? 1.f : 0.f;
                     }
                     need_any = need_any || need[rb];
                 }
@@ -834,8 +940,14 @@ __device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int
 // which stages each K/V tile into LDS once for 256 rows instead of twice for 128; it pays off
 // for long causal d = 128 heads (+2-3 % at N = 8192 and 131072) and loses where the grid is
 // small or the sequences short, so the host picks it only there.
+// Workgroups per CU the register budget is sized for: the d = 64, bf16-output kernel fits three
+// (at most 168 VGPRs, three waves per SIMD), which hides more latency; the others two, or one of
+// eight waves.
+template <int D, bool OUT_F32, int NW, bool DROP>
+constexpr int pipe_wgs_per_cu() { return NW == 8 ? 1 : (D == 64 && !OUT_F32 && !DROP) ? 3 : 2; }
+
 template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 4, bool DROP = false>
-__global__ void __launch_bounds__(64 * NW, NW == 8 ? 1 : 2) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(64 * NW, (pipe_wgs_per_cu<D, OUT_F32, NW, DROP>())) fa_fwd_bf16_pipe_kernel(FwdArgs a) {
     const TilePair tp = pair_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
     int Lk = a.N;
     if (PAD) {
