@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     FA_DTYPE_FP8_E4M3,
     FA_ERR_HIP,
     FA_ERR_INVALID_ARG,
+    FA_ERR_SCRATCH_LIMIT,
     FA_ERR_UNSUPPORTED,
     FA_MASK_CAUSAL,
     FA_MASK_KEY_PADDING,
@@ -33,6 +34,7 @@ from .binding import (  # noqa: F401
     forward_fp8,
     forward_varlen,
     load_library,
+    scratch_bytes,
     status_str,
     variant_count,
     varlen_workspace_size,

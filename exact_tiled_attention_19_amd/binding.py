@@ -21,6 +21,7 @@ FA_OK = 0
 FA_ERR_INVALID_ARG = 1
 FA_ERR_UNSUPPORTED = 2
 FA_ERR_HIP = 3
+FA_ERR_SCRATCH_LIMIT = 4
 
 FA_MASK_NONE = 0
 FA_MASK_CAUSAL = 1
@@ -51,6 +52,9 @@ SIGNATURES = {
     "fa_fwd_varlen": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _I,
                            _VP, ctypes.c_size_t, _I, _I, _VP]),
     "fa_fwd_varlen_workspace_size": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
+    "fa_fwd_varlen_noalloc": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I,
+                                   _I, _I, _I, _VP]),
+    "fa_scratch_bytes": (ctypes.c_size_t, []),
     "fa_bwd_dropout": (_I, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I, _I, _I, _I, ctypes.c_float, _I, _VP,
                             ctypes.c_float, ctypes.c_uint64, ctypes.c_uint32, _I, _I, _VP]),
     "fa_variant_count": (_I, []),
@@ -349,6 +353,18 @@ def fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, ma
                                         in_dtype, out_dtype, stream)
 
 
+def fa_fwd_varlen_noalloc(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, max_k, d, scale, mask_kind,
+                          causal_align, in_dtype, out_dtype, stream) -> int:
+    """Raw call of the allocation-free packed forward through the C ABI (pointers as ints or None)."""
+    return load_library().fa_fwd_varlen_noalloc(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, max_k,
+                                                d, ctypes.c_float(scale), mask_kind, causal_align, in_dtype,
+                                                out_dtype, stream)
+
+
+def scratch_bytes() -> int:
+    return int(load_library().fa_scratch_bytes())
+
+
 def varlen_workspace_size(B: int, H: int, max_seqlen_q: int, max_seqlen_k: int, d: int) -> int:
     return int(load_library().fa_fwd_varlen_workspace_size(B, H, max_seqlen_q, max_seqlen_k, d))
 
@@ -358,7 +374,8 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
                    max_seqlen_k: Optional[int] = None, *, scale: Optional[float] = None, causal: bool = False,
                    align: str = "bottom_right", out_dtype: Optional[torch.dtype] = None, return_lse: bool = True,
                    out: Optional[torch.Tensor] = None, lse_out: Optional[torch.Tensor] = None,
-                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                   workspace: Optional[torch.Tensor] = None,
+                   noalloc: bool = False) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Exact attention over a packed batch of sequences on the GPU: returns (O, LSE).
 
     q: [Tq, H, d], k, v: [Tk, H, d] contiguous bfloat16 device tensors (token-major).
@@ -369,6 +386,8 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
     align="bottom_right" and 0 for align="top_left".
     Returns O [Tq, H, d] (out_dtype, default bfloat16) and LSE [H, Tq] float32.
     workspace: optional uint8 device tensor of at least ``varlen_workspace_size(...)`` bytes.
+    noalloc: call fa_fwd_varlen_noalloc instead, whose workspace is the library's fixed device
+    array (no workspace is allocated or passed; pass ``out`` and ``lse_out`` to allocate nothing).
     """
     ts = (q, k, v, cu_seqlens_q, cu_seqlens_k)
     if not all(t.is_cuda for t in ts):
@@ -408,11 +427,20 @@ def forward_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens
             if lse_out.shape != (H, Tq) or lse_out.dtype != torch.float32 or not lse_out.is_contiguous():
                 raise ValueError("lse_out must be a contiguous float32 [H, Tq] tensor")
             lse = lse_out
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    if noalloc:
+        if workspace is not None:
+            raise ValueError("noalloc takes no workspace")
+        st = fa_fwd_varlen_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_k), B, H, Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d,
+                                   float(scale), FA_MASK_CAUSAL if causal else FA_MASK_NONE, _ALIGN_CODE[align],
+                                   FA_DTYPE_BF16, _DTYPE_CODE[out_dtype], stream)
+        _check(st)
+        return out, lse
     ws_bytes = varlen_workspace_size(B, H, max_seqlen_q, max_seqlen_k, d)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_given = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     st = fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, H,
                        Tq, Tk, int(max_seqlen_q), int(max_seqlen_k), d, float(scale),
                        FA_MASK_CAUSAL if causal else FA_MASK_NONE, _ALIGN_CODE[align], _ptr(workspace), ws_given,

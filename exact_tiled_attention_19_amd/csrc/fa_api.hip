@@ -1,10 +1,11 @@
 // C ABI of the fused attention forward (declared in include/fa.h): host-side validation,
-// kernel selection and launch.  No allocation, no synchronisation, no state except the
-// thread-local last HIP error.
+// kernel selection and launch.  No allocation and no synchronisation.  State: the thread-local
+// last HIP error, and for fa_fwd_varlen_noalloc a fixed device array with its per-device address.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/fa.h"
 #include "fa_fwd_bf16.h"
@@ -14,9 +15,47 @@
 #include "fa_bwd_bf16.h"
 #include "fa_decode_bf16.h"
 
+// Workspace of fa_fwd_varlen_noalloc: the partial states of the split-key decoding kernel.  The
+// largest plan needs bh * S * G * (d + 2) * 4 bytes with bh * S < 4096 (at most 2048 workgroups
+// are aimed for, and a split needs fewer than 2048 (sequence, head) pairs), G <= 4 and d <= 128:
+// 8,515,840 bytes, so 9 MiB holds every plan.  Each device the library runs on keeps its own
+// copy until the process ends.
+static __device__ __align__(256) unsigned char scratch[size_t{9} << 20];
+
 namespace {
 
 thread_local int g_last_hip_error = 0;
+
+constexpr size_t kScratchBytes = size_t{9} << 20;
+static_assert(sizeof(scratch) == kScratchBytes, "one size for the array and its checks");
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per device with that
+// device current.  In host code the name `scratch` only stands for the symbol and must never
+// reach a kernel: every use goes through the address returned here.
+int scratch_on_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return FA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            g_last_hip_error = static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+            return FA_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return FA_OK;
+}
 
 constexpr int kThreads = 256;  // 4 wave64s per workgroup
 
@@ -415,7 +454,7 @@ void pick_decode(int g, bool causal, DecKernel& main, DecKernel& merge) {
 int varlen_launch(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_q,
                   const int32_t* cu_k, int B, int H, int total_q, int total_k, int max_q, int max_k, int d,
                   float scale, int mask_kind, int causal_align, void* workspace, size_t workspace_bytes,
-                  int in_dtype, int out_dtype, void* stream) {
+                  int in_dtype, int out_dtype, void* stream, bool use_scratch = false) {
     // ---- validation (host only, before any HIP call) ----
     if (B < 0 || H < 0 || total_q < 0 || total_k < 0 || max_q < 0 || max_k < 0) return FA_ERR_INVALID_ARG;
     if (mask_kind != FA_MASK_NONE && mask_kind != FA_MASK_CAUSAL) return FA_ERR_INVALID_ARG;
@@ -436,7 +475,11 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
     if (static_cast<int64_t>(max_k) * row_bytes > 0xffffffffLL) return FA_ERR_INVALID_ARG;
     const bool causal = mask_kind == FA_MASK_CAUSAL;
     const DecodePlan plan = decode_plan(B, H, max_q, max_k, d);
-    if (plan.ws_bytes > 0) {
+    // the allocation-free entry point takes the library's fixed per-device array as the
+    // workspace (its address is fetched after every check has passed)
+    const bool from_scratch = use_scratch && plan.ws_bytes > 0;
+    if (from_scratch && plan.ws_bytes > kScratchBytes) return FA_ERR_SCRATCH_LIMIT;
+    if (plan.ws_bytes > 0 && !from_scratch) {
         if (!workspace || workspace_bytes < plan.ws_bytes || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
     }
     const int64_t bh = static_cast<int64_t>(B) * H;
@@ -464,6 +507,10 @@ int varlen_launch(const void* q, const void* k, const void* v, void* o, float* l
             if (ins[j] && overlaps(outs[i], out_sz[i], ins[j], in_sz[j])) return FA_ERR_INVALID_ARG;
         for (int j = i + 1; j < 3; ++j)
             if (outs[j] && overlaps(outs[i], out_sz[i], outs[j], out_sz[j])) return FA_ERR_INVALID_ARG;
+    }
+    if (from_scratch) {
+        const int status = scratch_on_current_device(&workspace);
+        if (status != FA_OK) return status;
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const float scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634074);
@@ -554,6 +601,17 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
                          out_dtype, stream);
 }
 
+int fa_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, const int32_t* cu_seqlens_q,
+                          const int32_t* cu_seqlens_k, int B, int H, int total_q, int total_k, int max_seqlen_q,
+                          int max_seqlen_k, int d, float scale, int mask_kind, int causal_align, int in_dtype,
+                          int out_dtype, void* stream) {
+    return varlen_launch(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, H, total_q, total_k, max_seqlen_q,
+                         max_seqlen_k, d, scale, mask_kind, causal_align, nullptr, 0, in_dtype, out_dtype, stream,
+                         true);
+}
+
+size_t fa_scratch_bytes(void) { return kScratchBytes; }
+
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
            float* delta, void* dq, void* dk, void* dv, int B, int H, int N, int d, float scale, int mask_kind,
            const int32_t* seqlens, int in_dtype, int grad_dtype, void* stream) {
@@ -606,6 +664,9 @@ const char* fa_status_str(int status) {
         case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
         case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: no kernel for this head width, dtype pair or variant";
         case FA_ERR_HIP: return "FA_ERR_HIP: kernel launch failed (see fa_last_hip_error)";
+        case FA_ERR_SCRATCH_LIMIT:
+            return "FA_ERR_SCRATCH_LIMIT: the call needs more workspace than the library's fixed scratch holds "
+                   "(use the entry point that takes a caller workspace)";
         default: return "unknown fa_status";
     }
 }

@@ -18,7 +18,8 @@
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library allocates,
  *     frees and synchronises nothing and keeps no state between calls except a thread-local
- *     copy of the last HIP error.  Work is enqueued on `stream` (a hipStream_t; NULL means the
+ *     copy of the last HIP error and, for fa_fwd_varlen_noalloc only, one fixed device array
+ *     per device (see there).  Work is enqueued on `stream` (a hipStream_t; NULL means the
  *     default stream) and the call returns without waiting for it.
  *   - Layout: Q, K, V and O are [B, H, N, d] contiguous row-major (d fastest); LSE is [B, H, N].
  *   - Masks (bit flags, FA_MASK_*): under FA_MASK_CAUSAL key j is visible to query i only when
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define FA_VERSION 10400 /* major*10000 + minor*100 + patch */
+#define FA_VERSION 10500 /* major*10000 + minor*100 + patch */
 
 typedef enum {
     FA_OK = 0,
@@ -51,7 +52,9 @@ typedef enum {
                                 seqlens, scale negative or not finite, misaligned pointer,
                                 O aliasing an input, size overflow */
     FA_ERR_UNSUPPORTED = 2,  /* valid arguments the library has no kernel for (d, dtype pair) */
-    FA_ERR_HIP = 3           /* the launch failed; fa_last_hip_error() gives the hipError_t */
+    FA_ERR_HIP = 3,          /* the launch failed; fa_last_hip_error() gives the hipError_t */
+    FA_ERR_SCRATCH_LIMIT = 4 /* fa_fwd_varlen_noalloc only: the call needs more workspace than the
+                                library's fixed scratch array holds (fa_scratch_bytes()) */
 } fa_status;
 
 enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL = 1, FA_MASK_KEY_PADDING = 2 };
@@ -239,6 +242,34 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
  * arguments; 0 for sizes fa_fwd_varlen would reject.
  */
 size_t fa_fwd_varlen_workspace_size(int B, int H, int max_seqlen_q, int max_seqlen_k, int d);
+
+/*
+ * fa_fwd_varlen_noalloc -- fa_fwd_varlen for callers that cannot allocate device memory: code
+ * recorded into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  It takes no
+ * workspace argument; the decoding kernel's partial states go to a fixed array inside the library
+ * instead (a `__device__` array of fa_scratch_bytes() = 9 MiB, which holds the workspace of every
+ * size fa_fwd_varlen accepts).  Each device keeps its own copy from the library's first call on it
+ * until the process ends; the call itself allocates nothing.
+ *
+ *   Arguments, layouts, visibility rule, kernels and results: those of fa_fwd_varlen with the same
+ *   arguments (bitwise equal outputs).  Validation as for fa_fwd_varlen, plus
+ *   FA_ERR_SCRATCH_LIMIT if fa_fwd_varlen_workspace_size() of the sizes exceeds fa_scratch_bytes().
+ *   The first call on a device looks up the array's address there (hipGetSymbolAddress) with that
+ *   device current; a failure of that lookup returns FA_ERR_HIP.
+ *
+ * Every call on one device shares that device's array, and the array keeps the last call's
+ * contents (each call writes every entry it later reads, so nothing needs clearing).  Calls that
+ * can overlap in time on one device -- on different streams, or from several host threads without
+ * ordering -- race on the array and may return wrong results: order them on one stream.
+ */
+int fa_fwd_varlen_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int H, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                          int d, float scale, int mask_kind, int causal_align,
+                          int in_dtype, int out_dtype, void* stream);
+
+/* Bytes of the fixed array fa_fwd_varlen_noalloc uses per device (9 MiB). */
+size_t fa_scratch_bytes(void);
 
 /*
  * fa_bwd_dropout -- gradients of fa_fwd_dropout's output with respect to Q, K and V, with the

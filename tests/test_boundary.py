@@ -349,3 +349,50 @@ def test_python_fp8_forward_rejects_bad_tensors():
     x = torch.zeros(1, 1, 4, 64, dtype=torch.uint8)
     with pytest.raises(ValueError):
         fa.forward_fp8(x, x, x)
+
+
+# ---- allocation-free packed entry point ----------------------------------------------------------
+
+def varlen_noalloc_call(q=VQ, k=VK, v=VV, o=VO, lse=VL, cu_q=VCQ, cu_k=VCK, B=2, H=2, total_q=64, total_k=64,
+                        max_q=32, max_k=32, d=64, scale=0.125, mask=0, align=fa.FA_ALIGN_BOTTOM_RIGHT, ind=BF16,
+                        outd=BF16, **_ignored):
+    return fa.binding.fa_fwd_varlen_noalloc(q, k, v, o, lse, cu_q, cu_k, B, H, total_q, total_k, max_q, max_k, d,
+                                            scale, mask, align, ind, outd, None)
+
+
+# every check of fa_fwd_varlen except those about the caller's workspace, which this entry point
+# does not take
+NOALLOC_INVALID = {n: a for n, a in VARLEN_INVALID.items() if "workspace" not in n}
+
+
+@pytest.mark.parametrize("name", sorted(NOALLOC_INVALID))
+def test_varlen_noalloc_invalid_argument_rejected_on_host(name):
+    assert varlen_noalloc_call(**NOALLOC_INVALID[name]) == fa.FA_ERR_INVALID_ARG, name
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_UNSUPPORTED))
+def test_varlen_noalloc_unsupported_rejected_on_host(name):
+    assert varlen_noalloc_call(**VARLEN_UNSUPPORTED[name]) == fa.FA_ERR_UNSUPPORTED, name
+
+
+@pytest.mark.parametrize("dims", [dict(B=0), dict(H=0), dict(total_q=0), dict(max_q=0)])
+def test_varlen_noalloc_empty_problem_is_a_noop(dims):
+    args = dict(q=None, k=None, v=None, o=None, lse=None, cu_q=None, cu_k=None)
+    args.update(dims)
+    assert varlen_noalloc_call(**args) == fa.FA_OK
+
+
+def test_scratch_holds_every_decode_plan():
+    """The fixed array (9 MiB) is at least the workspace of every size fa_fwd_varlen accepts: the
+    plan aims at 2048 workgroups, so (sequence, head) pairs times key ranges stay below 4096."""
+    cap = fa.binding.scratch_bytes()
+    assert cap == 9 << 20
+    lib = fa.load_library()
+    assert lib.fa_status_str(fa.binding.FA_ERR_SCRATCH_LIMIT).decode().startswith("FA_ERR_SCRATCH_LIMIT")
+    worst = 0
+    for d in (64, 128):
+        for mq in (1, 2, 4):
+            for bh in list(range(1, 130)) + list(range(130, 2100, 7)) + [2047, 2048, 2049, 4096, 100000]:
+                for mk in (512, 513, 1000, 4097, 8192, 65536, 131072, 1 << 20, 1 << 24):
+                    worst = max(worst, fa.varlen_workspace_size(1, bh, mq, mk, d))
+    assert 0 < worst <= cap, worst
