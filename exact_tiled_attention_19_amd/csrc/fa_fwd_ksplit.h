@@ -2,8 +2,8 @@
 // units, e.g. one head of a few thousand tokens).
 //
 // The NW waves of a workgroup (eight at d = 64, four at d = 128) share one 32-row query block
-// and divide its key tiles among themselves: wave w takes tiles w, w+NW, w+2NW, ...  Each wave
-// keeps the running maximum, sum and unnormalised accumulator of the online update
+// and divide its 64-key tiles among themselves: wave w takes tiles w, w+NW, w+2NW, ...  Each
+// wave keeps the running maximum, sum and unnormalised accumulator of the online update
 // ("FlashAttention Interview Questions: IO Complexity, Tiling, and Numerical Stability",
 // section "How can softmax be computed across tiles?") over its own keys, and at the end the NW
 // states are merged with the same rescaling: m = max_w m_w, l = sum_w 2^(m_w - m) l_w,
@@ -13,9 +13,11 @@
 //
 // Each wave stages its own K and V tiles in its own LDS region (global -> registers -> LDS,
 // the next tile's loads in flight while the current one is computed), so the tile loop needs
-// no workgroup barrier.  The probabilities enter the value product as two bf16 terms (P_hi +
-// P_lo) with a float32 output and in masked tiles, which hold every key of a row that sees
-// fewer than one tile of keys; otherwise as one bf16 term, as in the main kernel.
+// no workgroup barrier.  Every workgroup reads all of its head's keys and values, and the
+// per-CU load path and LDS traffic bound this kernel more than its MFMAs do.  The
+// probabilities enter the value product as two bf16 terms (P_hi + P_lo) with a float32 output
+// and in masked tiles, which hold every key of a row that sees fewer than one tile of keys;
+// otherwise as one bf16 term, as in the main kernel.
 //
 // F8: FP8 E4M3 inputs with per-tensor descales, as in the pipelined FP8 kernel: S on the 8-bit
 // MFMA with Q and K fragments taking the same byte -> dimension assignment, V widened to bf16
@@ -34,7 +36,7 @@ template <int D, bool CAUSAL, bool PAD, bool OUT_F32, int NW = 8, bool F8 = fals
 __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs a) {
     // NW waves; each walks every NW-th key tile
     constexpr int BM = 32;                     // query rows per workgroup (one MFMA block)
-    constexpr int BN = (D == 128 || NW == 8) ? 32 : 64;   // keys per tile (LDS: NW tiles)
+    constexpr int BN = 64;                     // keys per tile
     constexpr int RPW = 16 / NW;               // accumulator registers per block each wave finishes
     constexpr int ESZ = F8 ? 1 : 2;            // bytes per input element
     constexpr int KC = F8 ? D / 64 : D / 16;   // k-steps of the S MFMA
@@ -42,7 +44,9 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     constexpr int NDB = D / 32;                // 32-wide output blocks
     constexpr int PC = BN / 16;                // k-steps of the PV MFMA
     constexpr int KROWB = D * ESZ + 16;        // K row stride in LDS (bytes): 16-byte pad
-    constexpr int VSTR = D + 32;               // V row stride in LDS (bf16 elements): 64-byte pad
+    // V row stride in LDS (bf16 elements): a 64-byte pad, 32 bytes where eight waves' tiles
+    // would not fit the 160 KiB otherwise
+    constexpr int VSTR = D + ((NW == 8 && D * ESZ == 128) ? 16 : 32);
     constexpr int WBUFB = BN * KROWB + BN * VSTR * 2;   // bytes of one wave's K and V tiles
     constexpr int CPR = D * ESZ / 16;          // 16-byte input chunks per row
     constexpr int LDC = BN * CPR / 64;         // chunks per lane per tensor per tile
@@ -53,6 +57,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     static_assert(LDC * 64 == BN * CPR, "a tile must split evenly over the 64 lanes");
     static_assert((NW == 4 || NW == 8) && RPW * NW == 16, "each wave finishes whole register groups");
     static_assert(KROWB % 16 == 0 && WBUFB % 16 == 0, "16-byte LDS accesses stay aligned");
+    static_assert(SMEMB <= 160 * 1024, "the buffers fit the LDS");
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[SMEMB];
 
@@ -113,18 +118,25 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     uint16_t* const vs = (uint16_t*)(ks + BN * KROWB);          // and V tile (bf16)
     const unsigned char* const kg = (const unsigned char*)a.k + base * ESZ;
     const unsigned char* const vg = (const unsigned char*)a.v + base * ESZ;
-    // chunk ci = lane + 64 i of a tile: row ci / CPR, column chunk ci % CPR; rows past N are
-    // read from row N - 1 (they are masked)
-    u32x4 kr[LDC], vr[LDC];
+    // chunk ci = lane + 64 i of a tile: row ci / CPR, column chunk ci % CPR.  The loads go through
+    // buffer resources that start at the tile and end at key N, so rows past N read as zeros
+    // (they are masked) and the per-tile address arithmetic is scalar.
+    int goff[LDC];
+#pragma unroll
+    for (int i = 0; i < LDC; ++i) {
+        const int ci = lane + 64 * i;
+        goff[i] = (ci / CPR) * D * ESZ + (ci % CPR) * 16;
+    }
+    u32x4 kr[LDC], vr[LDC];   // the next tile on its way to LDS
     auto gload = [&](int tile) __attribute__((always_inline)) {
+        const int64_t toff = static_cast<int64_t>(tile) * BN * D * ESZ;
+        const int rec = (N - tile * BN) * D * ESZ;
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + toff), (short)0, rec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + toff), (short)0, rec, 0x00020000);
 #pragma unroll
         for (int i = 0; i < LDC; ++i) {
-            const int ci = lane + 64 * i;
-            const int row = ci / CPR;
-            int gr = tile * BN + row;
-            gr = gr < N ? gr : N - 1;
-            kr[i] = *(const u32x4*)(kg + (int64_t)gr * D * ESZ + (ci % CPR) * 16);
-            vr[i] = *(const u32x4*)(vg + (int64_t)gr * D * ESZ + (ci % CPR) * 16);
+            kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, goff[i], 0, 0));
+            vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, goff[i], 0, 0));
         }
     };
     auto swrite = [&]() __attribute__((always_inline)) {
@@ -164,15 +176,15 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
-    int t = wave;
-    if (t < n_tiles) {
-        gload(t);
-        swrite();
-    }
-    for (; t < n_tiles; t += NW) {
+    // wave w takes tiles w, w + NW, w + 2 NW, ...: R of them
+    const int n_rounds = (n_tiles + NW - 1) / NW;
+    const int R = wave < n_tiles - (n_rounds - 1) * NW ? n_rounds : n_rounds - 1;
+    auto tile_at = [&](int j) __attribute__((always_inline)) { return j * NW + wave; };
+    // one key tile: S, mask, online update, O += P V (its K and V are in this wave's LDS
+    // buffer).  MASKED: the tile holds a key past Lk or, under the causal mask, past a row.
+    auto tile_step = [&](int t, auto masked_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value;
         const int kv0 = t * BN;
-        const int tn = t + NW;
-        if (tn < n_tiles) gload(tn);   // in flight while this tile is computed
         f32x16 s[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -190,8 +202,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
             }
         }
         // accumulator register r of block kb holds key kv0 + 32kb + 8(r/4) + 4hh + r%4
-        const bool need_mask = (kv0 + BN > Lk) || (CAUSAL && kv0 + BN - 1 > q0);
-        if (need_mask) {
+        if constexpr (MASKED) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -207,9 +218,11 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = xor32_max(mx);
-        const float m_tile = (mx == kNegInf) ? kNegInf : mx * a.scale_log2;
+        // the scale is positive, so the largest score gives the largest scaled logit; a tile
+        // without masked keys has a finite maximum
+        const float m_tile = (MASKED && mx == kNegInf) ? kNegInf : mx * a.scale_log2;
         const float m_new = fmaxf(m_run, m_tile);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float m_use = (MASKED && m_new == kNegInf) ? 0.f : m_new;
         const float alpha = fast_exp2(m_run - m_use);
         float rs = 0.f;
 #pragma unroll
@@ -217,7 +230,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(fmaf(s[kb][r], a.scale_log2, -m_use));
-                if (need_mask) p = s[kb][r] == kNegInf ? 0.f : p;   // exact zeros, also when scale == 0
+                if constexpr (MASKED) p = s[kb][r] == kNegInf ? 0.f : p;   // exact zeros, also when scale == 0
                 s[kb][r] = p;
                 rs += p;
             }
@@ -249,12 +262,26 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
                 }
             }
         };
-        if (OUT_F32 || need_mask) pv(std::true_type{});
-        else pv(std::false_type{});
-        if (tn < n_tiles) swrite();   // this tile's reads have all returned (their MFMAs used them)
+        pv(std::integral_constant<bool, OUT_F32 || MASKED>{});
+    };
+    // Step i computes tile i from LDS while the loads of tile i+1 are in flight, then moves
+    // tile i+1 from registers to LDS
+    if (R > 0) {
+        gload(tile_at(0));
+        swrite();
+        for (int i = 0; i < R; ++i) {
+            const bool more = i + 1 < R;
+            if (more) gload(tile_at(i + 1));
+            const int t = tile_at(i);
+            if (t * BN + BN > Lk || (CAUSAL && t * BN + BN - 1 > q0)) tile_step(t, std::true_type{});
+            else tile_step(t, std::false_type{});
+            if (more) swrite();   // this tile's reads have all returned (their MFMAs used them)
+        }
     }
 
-    // merge.  LDS layout (floats): maxima [NW][32], sums [NW][32], accumulators [NW][64][16 NDB].
+    // merge.  LDS layout (floats): maxima [NW][32], sums [NW][32], accumulators
+    // [NW][4 NDB][64][4]: register group j (registers 4j .. 4j+3) of block db of wave v at
+    // [v][4 db + j][lane], so the 64 lanes of one access touch consecutive 16-byte slots.
     __syncthreads();   // every wave is done with its tile buffers
     float* const ms = reinterpret_cast<float*>(smem);
     float* const ls = ms + NW * 32;
@@ -268,7 +295,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            *(f32x4*)(as + (wave * 64 + lane) * 16 * NDB + 16 * db + 4 * j) =
+            *(f32x4*)(as + ((wave * 4 * NDB + 4 * db + j) * 64 + lane) * 4) =
                 f32x4{acc[db][4 * j], acc[db][4 * j + 1], acc[db][4 * j + 2], acc[db][4 * j + 3]};
     __syncthreads();
     // wave w finishes accumulator registers RPW w .. RPW w + RPW - 1 of every block: register r
@@ -296,7 +323,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
         for (int u = 0; u < RPW; ++u) o[u] = 0.f;
 #pragma unroll
         for (int v = 0; v < NW; ++v) {
-            const float* src = as + (v * 64 + lane) * 16 * NDB + 16 * db + r0;
+            const float* src = as + ((v * 4 * NDB + 4 * db + r0 / 4) * 64 + lane) * 4 + r0 % 4;
 #pragma unroll
             for (int u = 0; u < RPW; ++u) o[u] += sc[v] * src[u];
         }
