@@ -85,7 +85,9 @@ struct Launch {
 //      divide the keys --
 //      fa_fwd's choice when the grid of variant 0 would not fill the compute units
 //   5  the four-wave pipelined kernel of variant 0 at every size (no automatic choice)
-constexpr int kNumVariants = 6;
+//   6  key split with 16-row query blocks (16x16x32 MFMAs; 8 waves at d = 64, 4 at d = 128) --
+//      fa_fwd's choice for the smallest grids, where 32-row blocks leave compute units idle
+constexpr int kNumVariants = 7;
 // fa_fwd takes the key-split kernel when its own grid (one workgroup per 32 query rows) has at
 // most this many workgroups -- at most two (d = 64, eight waves) or a half (d = 128, four
 // waves) per compute unit of the 256 -- and there are at least this many keys per head.
@@ -95,6 +97,11 @@ constexpr int kNumVariants = 6;
 constexpr int64_t kKeySplitMaxWgsD64 = 512;
 constexpr int64_t kKeySplitMaxWgsD128 = 128;
 constexpr int kKeySplitMinN = 512;
+// ... and the 16-row key split (variant 6) when its grid, one workgroup per 16 query rows,
+// fits one workgroup per compute unit.  Measured: N = 4096 single heads 15.2 vs 18.3 us
+// (d = 64) and 35.4 vs 37.3 us (d = 128); with two 16-row workgroups per compute unit it was
+// slower (N = 4096, two heads, d = 64: 25.0 vs 18.3 us).
+constexpr int64_t kKeySplit16MaxWgs = 256;
 // fa_fwd takes the eight-wave kernel for causal d = 128 launches with at least this many
 // 256-row tiles (over all heads); smaller grids keep two 128-row workgroups per CU.
 constexpr int64_t kWave8MinTiles = 1024;
@@ -112,6 +119,9 @@ Launch pick_bf16_variant(int variant) {
         case 4:   // eight waves at d = 64; four at d = 128, where eight would not fit the registers
             if constexpr (D == 64) return {fa::fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32, 8>, 32, false, 512};
             else return {fa::fa_fwd_bf16_ksplit_kernel<D, CAUSAL, PAD, OUTF32, 4>, 32, false, 256};
+        case 6:
+            if constexpr (D == 64) return {fa::fa_fwd_bf16_ksplit16_kernel<D, CAUSAL, PAD, OUTF32, 8>, 16, false, 512};
+            else return {fa::fa_fwd_bf16_ksplit16_kernel<D, CAUSAL, PAD, OUTF32, 4>, 16, false, 256};
         default: return {nullptr, 0, false};
     }
 }
@@ -202,6 +212,8 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
     if (!drop && variant == 0 && in_dtype == FA_DTYPE_BF16 && N >= kKeySplitMinN) {
         const int64_t wgs = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 31) / 32);
         if (wgs <= (d == 64 ? kKeySplitMaxWgsD64 : kKeySplitMaxWgsD128)) variant = 4;
+        if (variant == 4 && static_cast<int64_t>(B) * H * ((static_cast<int64_t>(N) + 15) / 16) <= kKeySplit16MaxWgs)
+            variant = 6;
     }
     Launch L;
     if (drop) {

@@ -338,4 +338,296 @@ __global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit_kernel(FwdArgs 
     }
 }
 
+// Reductions across the four 16-lane rows of a wave (lanes j, j+16, j+32, j+48): v_permlane16_swap
+// with the same register as both operands leaves lane (l & ~16)'s value in the first result and
+// lane (l | 16)'s in the second, on every lane, so both lanes of a pair compute the same value.
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// The key split with 16-row query blocks, for the smallest grids: twice as many workgroups as
+// 32-row blocks give, so a single head of a few thousand tokens spreads over every compute
+// unit.  The same walk as above (wave w takes tiles w, w+NW, ..., merge of the NW states at
+// the end), on 16x16x32 bf16 MFMAs.  Lane l = 16 g + j works on query row j of the block:
+//   S^T = K Q^T per 16-key block kb and 32-wide slice c of d: the K operand is key 16 kb + j,
+//     dimensions 32 c + 8 g .. +8; Q's is row j, the same dimensions; accumulator register r
+//     holds key 16 kb + 4 g + r of row j.
+//   O^T += V^T P^T per 32-key chunk pc: the probabilities of blocks 2 pc and 2 pc + 1 that lane
+//     l holds (keys 32 pc + 4 g + e and 32 pc + 16 + 4 g + e, e = 0..3) are its P^T operand,
+//     and two LDS transpose reads give the V^T operand over the same keys for dimension
+//     16 db + j; accumulator register r holds dimension 16 db + 4 g + r of row j.
+template <int D, bool CAUSAL, bool PAD, bool OUT_F32, int NW>
+__global__ void __launch_bounds__(64 * NW, 1) fa_fwd_bf16_ksplit16_kernel(FwdArgs a) {
+    constexpr int BM = 16;                     // query rows per workgroup
+    constexpr int BN = 64;                     // keys per tile
+    constexpr int KC = D / 32;                 // k-steps of the S MFMA
+    constexpr int NKB = BN / 16;               // 16-key blocks per tile
+    constexpr int NDB = D / 16;                // 16-wide output blocks
+    constexpr int PC = BN / 32;                // k-steps of the PV MFMA
+    constexpr int RPW = 4 * NDB / NW;          // accumulator registers each wave finishes
+    constexpr int KROWB = D * 2 + 16;          // K row stride in LDS (bytes): 16-byte pad
+    constexpr int VSTR = D + 16;               // V row stride in LDS (bf16 elements): 32-byte pad
+    constexpr int WBUFB = BN * KROWB + BN * VSTR * 2;   // bytes of one wave's K and V tiles
+    constexpr int CPR = D * 2 / 16;            // 16-byte input chunks per row
+    constexpr int LDC = BN * CPR / 64;         // chunks per lane per tensor per tile
+    constexpr int MERGEB = (2 * NW * 16 + NW * NDB * 64 * 4) * 4;   // bytes of the merge state
+    constexpr int SMEMB = NW * WBUFB > MERGEB ? NW * WBUFB : MERGEB;
+    static_assert(LDC * 64 == BN * CPR, "a tile must split evenly over the 64 lanes");
+    static_assert(RPW * NW == 4 * NDB && (RPW <= 4 ? 4 % RPW == 0 : RPW % 4 == 0), "whole register groups");
+    static_assert(KROWB % 16 == 0 && WBUFB % 16 == 0, "16-byte LDS accesses stay aligned");
+    static_assert(SMEMB <= 160 * 1024, "the tile buffers fit the LDS");
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[SMEMB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15;
+    const int g = lane >> 4;
+
+    const TileCoord tc = tile_of(xcd_remap(blockIdx.x, a.total_wgs), a.n_qtiles, CAUSAL);
+    const int b = tc.bh / a.H;
+    const int N = a.N;
+    const int q0 = tc.qt * BM;
+    const int qrow = q0 + j;                   // the query row of this lane (every wave)
+    const int64_t base = (int64_t)tc.bh * N * D;
+
+    int Lk = N;
+    if (PAD) {
+        const int s = a.seqlens[b];
+        Lk = s < 0 ? 0 : (s > N ? N : s);
+    }
+    if (Lk == 0) {  // every key masked: O = 0, LSE = -inf (written by wave 0; lane row j, d in [g D/4, (g+1) D/4))
+        if (wave == 0 && qrow < N) {
+            if (g == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow] = kNegInf;
+#pragma unroll
+            for (int c = 0; c < D / 16; ++c) {
+                const int d0 = g * (D / 4) + 4 * c;
+                if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow * D + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow * D + d0) = u32x2{0u, 0u};
+            }
+        }
+        return;
+    }
+
+    int kv_end = Lk;
+    if (CAUSAL) kv_end = kv_end < q0 + BM ? kv_end : q0 + BM;
+    const int n_tiles = (kv_end + BN - 1) / BN;   // >= 1: key 0 is visible to every row
+
+    // Q^T operand of k-step c: Q[qrow][32c + 8g .. +8]
+    bf16x8 qf[KC];
+    {
+        const uint16_t* qp = (const uint16_t*)a.q + base + (int64_t)(qrow < N ? qrow : N - 1) * D + 8 * g;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+            qf[c] = *(const bf16x8*)(qp + 32 * c);
+            if (qrow >= N) qf[c] = bf16x8{};
+        }
+    }
+
+    unsigned char* const ks = smem + wave * WBUFB;              // this wave's K tile (bytes)
+    uint16_t* const vs = (uint16_t*)(ks + BN * KROWB);          // and V tile (bf16)
+    const unsigned char* const kg = (const unsigned char*)a.k + base * 2;
+    const unsigned char* const vg = (const unsigned char*)a.v + base * 2;
+    // chunk ci = lane + 64 i of a tile: row ci / CPR, column chunk ci % CPR, loaded through
+    // buffer resources that start at the tile and end at key N (rows past N read as zeros)
+    int goff[LDC];
+#pragma unroll
+    for (int i = 0; i < LDC; ++i) {
+        const int ci = lane + 64 * i;
+        goff[i] = (ci / CPR) * D * 2 + (ci % CPR) * 16;
+    }
+    u32x4 kr[LDC], vr[LDC];   // the next tile on its way to LDS
+    auto gload = [&](int tile) __attribute__((always_inline)) {
+        const int64_t toff = static_cast<int64_t>(tile) * BN * D * 2;
+        const int rec = (N - tile * BN) * D * 2;
+        const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kg + toff), (short)0, rec, 0x00020000);
+        const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vg + toff), (short)0, rec, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < LDC; ++i) {
+            kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, goff[i], 0, 0));
+            vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, goff[i], 0, 0));
+        }
+    };
+    auto swrite = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < LDC; ++i) {
+            const int ci = lane + 64 * i;
+            const int row = ci / CPR;
+            *(u32x4*)(ks + row * KROWB + (ci % CPR) * 16) = kr[i];
+            *(u32x4*)(vs + row * VSTR + (ci % CPR) * 8) = vr[i];
+        }
+        // the wave's other lanes read what this lane wrote: wait for the writes to complete
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+    };
+    // V^T operand of key chunk pc and output block db: the 16 lanes of row group g read the
+    // 4-key x 16-dimension blocks at keys 32pc + 4g (and + 16), dimensions 16db; lane j gets
+    // dimension 16db + j of those keys
+    auto vt_frag = [&](int pc, int db) __attribute__((always_inline)) -> bf16x8 {
+        const int row = 32 * pc + 4 * g + (j >> 2);
+        const int col = 16 * db + 4 * (j & 3);
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + row * VSTR + col)));
+        const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vs + (row + 16) * VSTR + col)));
+        return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+
+    float m_run = kNegInf;   // running maximum of scale*log2(e)*s over this wave's visible keys
+    float l_run = 0.f;       // this lane's running sum of 2^(.. - m_run) over its keys
+    f32x4 acc[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int n_rounds = (n_tiles + NW - 1) / NW;
+    const int R = wave < n_tiles - (n_rounds - 1) * NW ? n_rounds : n_rounds - 1;
+    auto tile_at = [&](int i) __attribute__((always_inline)) { return i * NW + wave; };
+    auto tile_step = [&](int t, auto masked_c) __attribute__((always_inline)) {
+        constexpr bool MASKED = decltype(masked_c)::value;
+        const int kv0 = t * BN;
+        f32x4 s[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                const bf16x8 kf = *(const bf16x8*)(ks + (16 * kb + j) * KROWB + 64 * c + 16 * g);
+                s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], s[kb], 0, 0, 0);
+            }
+        }
+        if constexpr (MASKED) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int key = kv0 + 16 * kb + 4 * g + r;
+                    const bool ok = key < Lk && (!CAUSAL || key <= qrow);
+                    s[kb][r] = ok ? s[kb][r] : kNegInf;
+                }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = xor32_max(xor16_max(mx));
+        // the scale is positive, so the largest score gives the largest scaled logit; a tile
+        // without masked keys has a finite maximum
+        const float m_tile = (MASKED && mx == kNegInf) ? kNegInf : mx * a.scale_log2;
+        const float m_new = fmaxf(m_run, m_tile);
+        const float m_use = (MASKED && m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float p = fast_exp2(fmaf(s[kb][r], a.scale_log2, -m_use));
+                if constexpr (MASKED) p = s[kb][r] == kNegInf ? 0.f : p;   // exact zeros, also when scale == 0
+                s[kb][r] = p;
+                rs += p;
+            }
+        l_run = alpha * l_run + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) acc[db] *= alpha;
+        constexpr bool SPLIT = OUT_F32 || MASKED;
+#pragma unroll
+        for (int pc = 0; pc < PC; ++pc) {
+            const f32x4 p0 = s[2 * pc], p1 = s[2 * pc + 1];
+            const u32x4 ph = {pack_bf16x2(p0[0], p0[1]), pack_bf16x2(p0[2], p0[3]),
+                              pack_bf16x2(p1[0], p1[1]), pack_bf16x2(p1[2], p1[3])};
+            u32x4 pl;
+            if constexpr (SPLIT) {
+                pl[0] = pack_bf16x2(p0[0] - bf16_lo_to_f32(ph[0]), p0[1] - bf16_hi_to_f32(ph[0]));
+                pl[1] = pack_bf16x2(p0[2] - bf16_lo_to_f32(ph[1]), p0[3] - bf16_hi_to_f32(ph[1]));
+                pl[2] = pack_bf16x2(p1[0] - bf16_lo_to_f32(ph[2]), p1[1] - bf16_hi_to_f32(ph[2]));
+                pl[3] = pack_bf16x2(p1[2] - bf16_lo_to_f32(ph[3]), p1[3] - bf16_hi_to_f32(ph[3]));
+            }
+#pragma unroll
+            for (int db = 0; db < NDB; ++db) {
+                const bf16x8 vf = vt_frag(pc, db);
+                acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8, ph), acc[db], 0, 0, 0);
+                if constexpr (SPLIT)
+                    acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, __builtin_bit_cast(bf16x8, pl), acc[db], 0, 0, 0);
+            }
+        }
+    };
+    // Step i computes tile i from LDS while the loads of tile i+1 are in flight, then moves
+    // tile i+1 from registers to LDS
+    if (R > 0) {
+        gload(tile_at(0));
+        swrite();
+        for (int i = 0; i < R; ++i) {
+            const bool more = i + 1 < R;
+            if (more) gload(tile_at(i + 1));
+            const int t = tile_at(i);
+            if (t * BN + BN > Lk || (CAUSAL && t * BN + BN - 1 > q0)) tile_step(t, std::true_type{});
+            else tile_step(t, std::false_type{});
+            if (more) swrite();   // this tile's reads have all returned (their MFMAs used them)
+        }
+    }
+
+    // merge.  LDS layout (floats): maxima [NW][16], sums [NW][16], accumulators
+    // [NW][NDB][64][4] (block db of wave v at [v][db][lane], lane-contiguous 16-byte slots)
+    __syncthreads();   // every wave is done with its tile buffers
+    float* const ms = reinterpret_cast<float*>(smem);
+    float* const ls = ms + NW * 16;
+    float* const as = ls + NW * 16;
+    const float l_tot = xor32_sum(xor16_sum(l_run));
+    if (g == 0) {
+        ms[wave * 16 + j] = m_run;
+        ls[wave * 16 + j] = l_tot;
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) *(f32x4*)(as + ((wave * NDB + db) * 64 + lane) * 4) = acc[db];
+    __syncthreads();
+    float m = kNegInf;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) m = fmaxf(m, ms[v * 16 + j]);
+    float sc[NW];
+    float l = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+        const float mv = ms[v * 16 + j];
+        sc[v] = mv == kNegInf ? 0.f : fast_exp2(mv - m);   // a wave without keys adds nothing
+        l += sc[v] * ls[v * 16 + j];
+    }
+    if (qrow >= N) return;
+    if (wave == 0 && g == 0 && a.lse) a.lse[(int64_t)tc.bh * N + qrow] = (m + __log2f(l)) * kLn2;
+    const float inv_l = 1.0f / l;
+    // wave w finishes accumulator registers x = RPW w .. RPW w + RPW - 1 (register x: block
+    // x / 4, dimension 16 (x / 4) + 4 g + x % 4), in runs of up to four adjacent dimensions
+    constexpr int RUN = RPW < 4 ? RPW : 4;
+#pragma unroll
+    for (int gi = 0; gi < RPW / RUN; ++gi) {
+        const int x0 = RPW * wave + RUN * gi;
+        const int db = x0 / 4, r0 = x0 % 4;
+        float o[RUN];
+#pragma unroll
+        for (int u = 0; u < RUN; ++u) o[u] = 0.f;
+#pragma unroll
+        for (int v = 0; v < NW; ++v) {
+            const float* src = as + ((v * NDB + db) * 64 + lane) * 4 + r0;
+#pragma unroll
+            for (int u = 0; u < RUN; ++u) o[u] += sc[v] * src[u];
+        }
+        const int d0 = 16 * db + 4 * g + r0;
+        float* const of = (float*)a.o + base + (int64_t)qrow * D + d0;
+        uint16_t* const ob = (uint16_t*)a.o + base + (int64_t)qrow * D + d0;
+        if constexpr (RUN == 4) {
+            if (OUT_F32) *(f32x4*)of = f32x4{o[0] * inv_l, o[1] * inv_l, o[2] * inv_l, o[3] * inv_l};
+            else *(u32x2*)ob = u32x2{pack_bf16x2(o[0] * inv_l, o[1] * inv_l), pack_bf16x2(o[2] * inv_l, o[3] * inv_l)};
+        } else {
+            if (OUT_F32) *(f32x2*)of = f32x2{o[0] * inv_l, o[1] * inv_l};
+            else *(uint32_t*)ob = pack_bf16x2(o[0] * inv_l, o[1] * inv_l);
+        }
+    }
+}
+
 }  // namespace fa

@@ -5,7 +5,7 @@ capture its launches, as serving loops do.  Each graph is replayed several times
 work (the outputs overwritten with NaN) and a device synchronisation between replays; every
 replay must reproduce the eager result bitwise (same kernels on the same inputs).
 
-Covered: the forward's pipelined kernel and its key-split kernel for small grids, the FP8
+Covered: the forward's pipelined kernel and its two key-split kernels for small grids, the FP8
 forward, a decoding step of the packed forward (split-key kernel, merge, caller workspace) and
 the backward pass.
 """
@@ -50,8 +50,8 @@ def _capture_and_replay(fn, outs, replays=4):
             assert torch.equal(o, e), f"replay {i} differs from the eager result"
 
 
-@pytest.mark.parametrize("shape", [(2, 4, 1024, 128, True), (1, 1, 4096, 64, False)],
-                         ids=["pipelined", "key-split"])
+@pytest.mark.parametrize("shape", [(2, 4, 1024, 128, True), (1, 1, 4096, 64, False), (1, 4, 2048, 64, True)],
+                         ids=["pipelined", "key-split-16-rows", "key-split-32-rows"])
 def test_forward_in_graph(shape):
     B, H, N, d, causal = shape
     q, k, v, _ = W.random_qkv(B, H, N, d, torch.bfloat16, seed=81)

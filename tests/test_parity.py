@@ -54,7 +54,7 @@ def test_sweep_bf16(N, d, mask):
                                   out_dtype=out_dtype, label=label))
 
 
-@pytest.mark.parametrize("variant", range(1, 6))
+@pytest.mark.parametrize("variant", range(1, 7))
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_variants_bf16(variant, d, mask):
@@ -71,14 +71,15 @@ def test_variants_bf16(variant, d, mask):
                                   out_dtype=out_dtype, variant=variant, label=label))
 
 
-@pytest.mark.parametrize("variant", [4, 5])
+@pytest.mark.parametrize("variant", [4, 5, 6])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("N", [1, 17, 64, 65, 129, 300, 1000, 2100])
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_sweep_small_grid_kernels(N, d, mask, variant):
-    """Variant 4 (key split across the waves of a workgroup; fa_fwd's choice for grids smaller
-    than the chip) and variant 5 (the four-wave pipelined kernel, which fa_fwd would replace by
-    variant 4 at these sizes) over ragged sizes, every mask, both output types."""
+    """Variants 4 and 6 (key split across the waves of a workgroup over 32- and 16-row query
+    blocks; fa_fwd's choices for grids smaller than the chip) and variant 5 (the four-wave
+    pipelined kernel, which fa_fwd would replace at these sizes) over ragged sizes, every mask,
+    both output types."""
     causal, pad = MASKS[mask]
     B, H = 1, 2
     q, k, v, _ = W.random_qkv(B, H, N, d, BF16, seed=4000 + N + d)
@@ -161,7 +162,7 @@ def test_workload_c4_sampled_rows():
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("variant", [4, 5])
+@pytest.mark.parametrize("variant", [4, 5, 6])
 def test_small_grid_kernels_empty_and_clamped_lengths(variant):
     """Key padding with seqlens 0, negative (clamped to 0) and above N (clamped to N) through
     the key-split kernel and the four-wave kernel: O = 0 and LSE = -inf for the empty batch
