@@ -57,11 +57,15 @@ struct BwdArgs {
 constexpr float kLog2e = 1.4426950408889634074f;
 
 // XOR swizzle of the 16-byte chunk index within a tile row in LDS.  Rows are read both whole
-// (16 bytes per lane) and with the 4 x 16 transpose read; the swizzle is a function of the row
-// alone, so both read kinds address the same layout.
+// (16 bytes per lane, 16 consecutive rows per pass of 16 lanes) and with the 4 x 16 transpose
+// read (4 consecutive rows x 4 consecutive chunks per 32 lanes); the swizzle is a function of
+// the row alone, so both read kinds address the same layout.  Bits 2-3 of the swizzle separate
+// the 4 rows of a transpose read; the remaining bits make the 16 rows of a whole-row pass land
+// on distinct banks (at d = 128 a row spans all 64 banks; at d = 64 two rows do, so only the 8
+// rows of one parity must differ).
 template <int D>
 __device__ __forceinline__ int bwd_swz(int row) {
-    return D == 128 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+    return D == 128 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
 }
 
 template <int D>
@@ -84,8 +88,9 @@ __device__ __forceinline__ bf16x8 bwd_trfrag(const unsigned char* tile, int l32,
     const int vrow = 4 * hh + ((l32 & 15) >> 2);
     const int chunk = 4 * db + ((l32 & 16) >> 3) + ((l32 & 3) >> 1);
     const unsigned char* p0 = tile + (16 * pc + vrow) * (D * 2) + ((chunk ^ bwd_swz<D>(vrow)) << 4) + (l32 & 1) * 8;
+    const unsigned char* p1 = tile + (16 * pc + vrow + 8) * (D * 2) + ((chunk ^ bwd_swz<D>(vrow + 8)) << 4) + (l32 & 1) * 8;
     const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0));
-    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0 + 8 * D * 2)));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1));
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
