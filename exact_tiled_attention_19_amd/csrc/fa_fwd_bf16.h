@@ -67,6 +67,12 @@ struct FwdArgs {
     float drop_keep_scale;       // 256 / (256 - drop_t)
     // 8-bit inputs only: the value tensor's descale, applied to the output
     float v_descale;
+    // packed sequences with the keys split into ranges (split tile kernel and its merge): the
+    // caller's workspace holds every range's float32 output rows and log-sum-exps
+    float* ws_o;           // [n_ranges][B][H][max_q][d]
+    float* ws_lse;         // [n_ranges][B][H][max_q]
+    int n_ranges;          // key ranges per (sequence, head)
+    int range_keys;        // keys per range (a multiple of the key tile)
 };
 
 using FwdKernelFn = void (*)(FwdArgs);
@@ -80,13 +86,15 @@ __attribute__((visibility("hidden"))) FwdKernelFn pick_fp8_kernel(int d, int mas
 
 // Where the rows of one head of one sequence live, and which keys its queries may see.
 struct SeqGeom {
-    int64_t qbase;  // element offset of query (and output) row 0
+    int64_t qbase;  // element offset of query row 0
     int64_t kbase;  // element offset of key (and value) row 0
     int64_t lbase;  // index of row 0's log-sum-exp
+    int64_t obase;  // element offset of output row 0
     int Lq;         // query rows
     int Lk;         // keys
     int dlt;        // causal mask: key j is visible to query row i iff j <= i + dlt
-    int rse;        // elements between consecutive rows
+    int rse;        // elements between consecutive input rows
+    int orse;       // elements between consecutive output rows
 };
 
 // Sequence b, head h of a packed batch.  Offsets are clamped into the tensors, so any
@@ -106,6 +114,8 @@ __device__ __forceinline__ SeqGeom varlen_geom(const FwdArgs& a, int b, int h, i
     g.qbase = ((int64_t)qs * a.H + h) * D;
     g.kbase = ((int64_t)ks * a.H + h) * D;
     g.lbase = (int64_t)h * a.total_q + qs;
+    g.obase = g.qbase;
+    g.orse = g.rse;
     return g;
 }
 

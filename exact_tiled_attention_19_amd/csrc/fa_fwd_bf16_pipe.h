@@ -124,8 +124,10 @@ __device__ __forceinline__ unsigned char* pipe_lds() {
 // BN keys).  NW: waves per workgroup (4, or 8 for one 256-row workgroup per CU).  DROP:
 // dropout on the probabilities that enter the value product (the row sums, and so O's
 // normaliser and the log-sum-exp, take them undropped; kept ones are scaled in the epilogue).
+// STF32: the output rows are stored as float32 whatever OUT_F32 says about the probabilities'
+// precision (the key ranges of the split packed kernel, merged and rounded afterwards).
 template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL = false, bool SPLITM = false, int NW = 4,
-          bool DROP = false, bool F8 = false>
+          bool DROP = false, bool F8 = false, bool STF32 = OUT_F32>
 __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, const SeqGeom& sg = SeqGeom{}) {
     constexpr int WR = 32 * RB;             // query rows per wave
     constexpr int BM = NW * WR;             // query rows per workgroup
@@ -180,7 +182,9 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
     const int64_t base = VL ? sg.qbase : (int64_t)tc.bh * N * D;   // query / output rows
     const int64_t kbase = VL ? sg.kbase : base;                       // key / value rows
     const int64_t lbase = VL ? sg.lbase : (int64_t)tc.bh * N;         // log-sum-exp entries
+    const int64_t obase = VL ? sg.obase : base;                       // output rows
     const int RSE = VL ? sg.rse : D;           // elements between consecutive rows
+    const int ORSE = VL ? sg.orse : D;         // the same for the output
     const int RSB = RSE * ESZ;                 // the same in bytes (inputs)
     const int dlt = VL ? sg.dlt : 0;           // causal: key j visible to row i iff j <= i + dlt
 
@@ -201,8 +205,8 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int d0 = 32 * db + 8 * j + 4 * hh;
-                    if (OUT_F32) *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * RSE + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
-                    else *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * RSE + d0) = u32x2{0u, 0u};
+                    if (STF32) *(f32x4*)((float*)a.o + obase + (int64_t)qrow[rb] * ORSE + d0) = f32x4{0.f, 0.f, 0.f, 0.f};
+                    else *(u32x2*)((uint16_t*)a.o + obase + (int64_t)qrow[rb] * ORSE + d0) = u32x2{0u, 0u};
                 }
         }
         return;
@@ -905,10 +909,10 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
                 const float o1 = acc[rb][db][4 * jj + 1] * inv_l;
                 const float o2 = acc[rb][db][4 * jj + 2] * inv_l;
                 const float o3 = acc[rb][db][4 * jj + 3] * inv_l;
-                if (OUT_F32) {
-                    *(f32x4*)((float*)a.o + base + (int64_t)qrow[rb] * RSE + d0) = f32x4{o0, o1, o2, o3};
+                if (STF32) {
+                    *(f32x4*)((float*)a.o + obase + (int64_t)qrow[rb] * ORSE + d0) = f32x4{o0, o1, o2, o3};
                 } else {
-                    *(u32x2*)((uint16_t*)a.o + base + (int64_t)qrow[rb] * RSE + d0) =
+                    *(u32x2*)((uint16_t*)a.o + obase + (int64_t)qrow[rb] * ORSE + d0) =
                         u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
                 }
             }
@@ -921,16 +925,16 @@ __device__ __forceinline__ void pipe_tile(const FwdArgs& a, int bh, int qt, cons
 // instantiation otherwise, so the diagonal tiles of the long rows pay nothing.  Without the
 // causal mask the only masked tile is the ragged end of the keys, and it always takes them.
 template <int D, int BN, int RB, bool CAUSAL, bool PAD, bool OUT_F32, bool VL, int NW = 4, bool DROP = false,
-          bool F8 = false>
+          bool F8 = false, bool STF32 = OUT_F32>
 __device__ __forceinline__ void pipe_tile_dispatch(const FwdArgs& a, int bh, int qt, int Lk, int dlt,
                                                    const SeqGeom& sg) {
     constexpr int BM = NW * 32 * RB;
     if constexpr (OUT_F32 || !CAUSAL) {
-        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP, F8>(a, bh, qt, sg);
+        pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP, F8, STF32>(a, bh, qt, sg);
     } else {
         const bool few = Lk < BN || qt * BM + 1 + dlt < BN;
-        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP, F8>(a, bh, qt, sg);
-        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW, DROP, F8>(a, bh, qt, sg);
+        if (few) pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, true, NW, DROP, F8, STF32>(a, bh, qt, sg);
+        else pipe_tile<D, BN, RB, CAUSAL, PAD, OUT_F32, VL, false, NW, DROP, F8, STF32>(a, bh, qt, sg);
     }
 }
 
@@ -1019,6 +1023,91 @@ __global__ void __launch_bounds__(256, 2) fa_fwd_bf16_varlen_kernel(FwdArgs a) {
         __syncthreads();
         pipe_tile_dispatch<D, BN, RB, CAUSAL, true, OUT_F32, true>(a, bh, qt1, sg.Lk, CAUSAL ? sg.dlt : 0, sg);
     }
+}
+
+
+// Packed sequences whose tiles alone would leave most of the chip idle (a few long prefill
+// chunks, a single long sequence): the keys of every (sequence, head) are split into
+// a.n_ranges ranges of a.range_keys keys, and one workgroup runs query tile qt of head bh over
+// the keys of range r only -- the same tile code on a shifted key window (key j of the range
+// is key r * range_keys + j of the sequence, and the causal offset moves with it).  Each range
+// writes its float32 output rows and its log-sum-exp to the caller's workspace; a row that
+// sees no key of the range gets O = 0 and LSE = -inf there.  The probabilities follow the
+// final output type's precision rule (OUT_F32).  fa_fwd_varlen_merge_kernel then combines the
+// ranges with the online update's rescaling.  Work item: query tile it (heaviest first under
+// the causal mask) of the pair (head bh, range r), numbered bh * n_ranges + r; the tiles of one
+// pair run on one XCD, which reads that range's keys into its L2 once, and the ranges of one
+// head spread over the XCDs.
+template <int D, int BN, bool CAUSAL, bool OUT_F32>
+__global__ void __launch_bounds__(256, 2) fa_fwd_bf16_varlen_split_kernel(FwdArgs a) {
+    constexpr int BM = 128;
+    const int S = a.n_ranges;
+    const HeadItem hi = head_item_xcd(blockIdx.x, a.B * a.H * S, a.n_qtiles);
+    if (hi.bh < 0) return;
+    const int bh = hi.bh / S;
+    const int r = hi.bh - bh * S;
+    const int b = bh / a.H;
+    const int h = bh - b * a.H;
+    const int itq = hi.it;
+    const SeqGeom sg = varlen_geom(a, b, h, D);
+    const int n = (sg.Lq + BM - 1) / BM;
+    if (itq >= n) return;
+    const int qt = CAUSAL ? n - 1 - itq : itq;
+    const int k_lo = r * a.range_keys;
+    const int k_hi = sg.Lk < k_lo + a.range_keys ? sg.Lk : k_lo + a.range_keys;
+    SeqGeom rg = sg;
+    rg.kbase = sg.kbase + (int64_t)k_lo * sg.rse;
+    rg.Lk = k_hi > k_lo ? k_hi - k_lo : 0;
+    rg.dlt = sg.dlt - k_lo;
+    const int64_t slot = ((int64_t)r * a.B + b) * a.H + h;   // (range, sequence, head)
+    rg.obase = slot * a.max_q * D;
+    rg.orse = D;
+    rg.lbase = slot * a.max_q;
+    FwdArgs ar = a;
+    ar.o = a.ws_o;
+    ar.lse = a.ws_lse;
+    pipe_tile_dispatch<D, BN, 1, CAUSAL, true, OUT_F32, true, 4, false, false, true>(ar, bh, qt, rg.Lk, CAUSAL ? rg.dlt : 0, rg);
+}
+
+// Combines the key ranges of fa_fwd_varlen_split_kernel: for row i of sequence b, head h,
+// LSE = ln sum_r exp(LSE_r) and O = sum_r exp(LSE_r - LSE) O_r, the ranges taken in order (so
+// the result is the same on every run).  A row that sees no key at all keeps O = 0 and
+// LSE = -inf.  One thread per four columns of a row; rows past a sequence's length are skipped.
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(256) fa_fwd_varlen_merge_kernel(FwdArgs a) {
+    constexpr int TPR = D / 4;                       // threads per row
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row_id = gid / TPR;                // ((b * H + h) * max_q + i)
+    const int c = (int)(gid % TPR);
+    const int i = (int)(row_id % a.max_q);
+    const int64_t bh = row_id / a.max_q;
+    if (bh >= (int64_t)a.B * a.H) return;
+    const int b = (int)(bh / a.H);
+    const int h = (int)(bh - (int64_t)b * a.H);
+    const SeqGeom sg = varlen_geom(a, b, h, D);
+    if (i >= sg.Lq) return;
+    const int S = a.n_ranges;
+    const int64_t rstride = (int64_t)a.B * a.H * a.max_q;   // rows between consecutive ranges
+    float m = kNegInf;
+    for (int r = 0; r < S; ++r) m = fmaxf(m, a.ws_lse[r * rstride + row_id]);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    float lse = kNegInf;
+    if (m != kNegInf) {
+        float wsum = 0.f;
+        for (int r = 0; r < S; ++r) {
+            const float lr = a.ws_lse[r * rstride + row_id];
+            const float w = lr == kNegInf ? 0.f : fast_exp2((lr - m) * 1.4426950408889634f);
+            wsum += w;
+            const f32x4 x = *(const f32x4*)(a.ws_o + (r * rstride + row_id) * D + 4 * c);
+            o += w * x;
+        }
+        o *= 1.f / wsum;
+        lse = m + __logf(wsum);
+    }
+    const int64_t off = sg.obase + (int64_t)i * sg.orse + 4 * c;
+    if (OUT_F32) *(f32x4*)((float*)a.o + off) = o;
+    else *(u32x2*)((uint16_t*)a.o + off) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    if (c == 0 && a.lse) a.lse[sg.lbase + i] = lse;
 }
 
 }  // namespace fa

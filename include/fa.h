@@ -226,8 +226,12 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
  * Kernels: when max_seqlen_q <= 4 (decoding shapes) the keys of every (sequence, head) are cut
  * into ranges processed by separate workgroups with fp32 vector arithmetic (the work is bound
  * by the K/V stream), and a second kernel merges the ranges' running statistics; otherwise the
- * tiled MFMA kernel of fa_fwd runs on the packed layout.  No atomics: results are identical
- * from run to run.  Validation is done on the host before any HIP call; B, H, total_q or
+ * tiled MFMA kernel of fa_fwd runs on the packed layout.  When those tiles would number at most
+ * 128 (e.g. one long sequence) and max_seqlen_k >= 1024, each (sequence, head)'s keys are cut
+ * into ranges there too: every range runs the tiled kernel into the workspace (float32 rows and
+ * log-sum-exps), and a second kernel merges the ranges, with the same rescaling, into o and
+ * lse.  No atomics, and the ranges merge in a fixed order: results are identical from run to
+ * run.  Validation is done on the host before any HIP call; B, H, total_q or
  * max_seqlen_q equal to 0 is a no-op.  Returns an fa_status.
  */
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -239,21 +243,25 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* l
 
 /*
  * Bytes of workspace fa_fwd_varlen needs for these sizes (0: none).  A pure function of its
- * arguments; 0 for sizes fa_fwd_varlen would reject.
+ * arguments; 0 for sizes fa_fwd_varlen would reject.  Decoding shapes with their keys split:
+ * B*H*ranges*rows*(d+2)*4 bytes (rows 1 or 4).  Prefill shapes with their keys split:
+ * ranges*B*H*max_seqlen_q*(d+1)*4 bytes.
  */
 size_t fa_fwd_varlen_workspace_size(int B, int H, int max_seqlen_q, int max_seqlen_k, int d);
 
 /*
  * fa_fwd_varlen_noalloc -- fa_fwd_varlen for callers that cannot allocate device memory: code
  * recorded into a HIP graph, tight serving loops, harnesses that forbid hipMalloc.  It takes no
- * workspace argument; the decoding kernel's partial states go to a fixed array inside the library
+ * workspace argument; the key ranges' partial states go to a fixed array inside the library
  * instead (a `__device__` array of fa_scratch_bytes() = 9 MiB, which holds the workspace of every
- * size fa_fwd_varlen accepts).  Each device keeps its own copy from the library's first call on it
- * until the process ends; the call itself allocates nothing.
+ * decoding size fa_fwd_varlen accepts).  Each device keeps its own copy from the library's first
+ * call on it until the process ends; the call itself allocates nothing.
  *
- *   Arguments, layouts, visibility rule, kernels and results: those of fa_fwd_varlen with the same
- *   arguments (bitwise equal outputs).  Validation as for fa_fwd_varlen, plus
- *   FA_ERR_SCRATCH_LIMIT if fa_fwd_varlen_workspace_size() of the sizes exceeds fa_scratch_bytes().
+ *   Arguments, layouts, visibility rule and results: those of fa_fwd_varlen with the same
+ *   arguments.  Kernels: those of fa_fwd_varlen (bitwise equal outputs), except that a prefill
+ *   shape whose split keys would need more than the array runs the tiled kernel unsplit (equal
+ *   within rounding, not bitwise).  Validation as for fa_fwd_varlen, plus FA_ERR_SCRATCH_LIMIT if
+ *   a decoding shape's fa_fwd_varlen_workspace_size() exceeds fa_scratch_bytes().
  *   The first call on a device looks up the array's address there (hipGetSymbolAddress) with that
  *   device current; a failure of that lookup returns FA_ERR_HIP.
  *

@@ -211,10 +211,21 @@ def test_varlen_empty_problem_is_a_noop(dims):
 
 
 def test_varlen_workspace_size():
-    """Workspace only for decoding shapes (<= 4 query rows) whose key ranges are split; its size
-    is B*H*ranges*rows*(d+2)*4 bytes, a pure function of the sizes."""
+    """Workspace only where keys are split into ranges: decoding shapes (<= 4 query rows),
+    B*H*ranges*rows*(d+2)*4 bytes; and prefill shapes whose 128-row tiles number at most 128
+    with at least 1024 keys, ranges*B*H*max_q*(d+1)*4 bytes.  A pure function of the sizes."""
     ws = fa.varlen_workspace_size
-    assert ws(4, 16, 5, 8192, 128) == 0                 # prefill shape: tile kernel
+    assert ws(64, 64, 300, 8192, 128) == 0              # prefill, 12288 tiles fill the chip: unsplit
+    assert ws(4, 16, 512, 8192, 128) == 0               # prefill, 256 tiles (one workgroup per CU): unsplit
+    assert ws(4, 16, 300, 1000, 128) == 0               # prefill, too few keys to split
+    for B, H, mq, mk, d in [(4, 16, 5, 8192, 128), (1, 2, 8192, 8192, 128), (1, 1, 4096, 4096, 64), (2, 3, 300, 1100, 64)]:
+        n = ws(B, H, mq, mk, d)
+        unit = B * H * mq * (d + 1) * 4
+        tiles = B * H * -(-mq // 128)
+        assert n > 0 and n % unit == 0, (B, H, mq, mk, d, n)
+        S = n // unit
+        assert 2 <= S <= min(16, mk // 512, -(-512 // tiles)), S
+        assert ws(B, H, mq, mk, d) == n                 # deterministic
     assert ws(64, 64, 1, 8192, 128) == 0                # 4096 heads fill the chip: one range
     assert ws(4, 16, 1, 500, 128) == 0                  # too few keys to split
     assert ws(-1, 16, 1, 8192, 128) == 0 and ws(4, 16, 1, 8192, 96) == 0

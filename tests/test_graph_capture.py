@@ -6,8 +6,8 @@ work (the outputs overwritten with NaN) and a device synchronisation between rep
 replay must reproduce the eager result bitwise (same kernels on the same inputs).
 
 Covered: the forward's pipelined kernel and its two key-split kernels for small grids, the FP8
-forward, a decoding step of the packed forward (split-key kernel, merge, caller workspace) and
-the backward pass.
+forward, a decoding step of the packed forward (split-key kernel, merge, caller workspace), a
+packed prefill with its keys split into ranges (split tile kernel, merge) and the backward pass.
 """
 
 import pytest
@@ -80,6 +80,19 @@ def test_decode_step_in_graph():
     assert ws_bytes > 0   # several key ranges: the split-key kernel and the merge both run
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
     # the longest lengths are passed, so the binding reads nothing back from the device
+    _capture_and_replay(lambda: fa.forward_varlen(qp, kp, vp, cq, ck, max(lq), max(lk), causal=True, out=o,
+                                                  lse_out=lse, workspace=ws), [o, lse])
+
+
+def test_split_prefill_in_graph():
+    lq, lk, H, d = [300, 77], [3000, 1100], 2, 128
+    qp, kp, vp, cq, ck = W.random_packed(lq, lk, H, d, torch.bfloat16, seed=86)
+    qp, kp, vp, cq, ck = (t.to(DEV) for t in (qp, kp, vp, cq, ck))
+    o = torch.empty(sum(lq), H, d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(H, sum(lq), dtype=torch.float32, device=DEV)
+    ws_bytes = fa.varlen_workspace_size(len(lq), H, max(lq), max(lk), d)
+    assert ws_bytes > 0   # the keys are split into ranges: the split tile kernel and its merge run
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
     _capture_and_replay(lambda: fa.forward_varlen(qp, kp, vp, cq, ck, max(lq), max(lk), causal=True, out=o,
                                                   lse_out=lse, workspace=ws), [o, lse])
 

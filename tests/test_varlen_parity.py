@@ -7,8 +7,9 @@ Tolerances are those of the square forward: float32 output |dO| <= 2e-4, bf16 ou
 max(1e-2, half a bf16 ulp + 1e-3) per element, LSE <= 1e-4.
 
 Cases: ragged packed batches with empty sequences, more queries than keys and fewer, both
-causal alignments and no mask; the tile kernel (more than 4 query rows) and the decoding kernel
-(at most 4) with one key range and with several merged ranges; the full-size decoding,
+causal alignments and no mask; the tile kernel (more than 4 query rows) unsplit and with its
+keys split into ranges merged afterwards (small grids); the decoding kernel (at most 4 query
+rows) with one key range and with several merged ranges; the full-size decoding,
 chunked-prefill and packed-mix workloads; isolation between neighbouring sequences; bitwise
 determinism; and workspace reuse.
 """
@@ -92,6 +93,29 @@ def test_decode_kernel(shape, mask, d, out_dtype):
     check(lq, lk, 3, d, mask, out_dtype, seed=200 + d, label=f"decode {shape} d={d} {mask} {out_dtype}")
 
 
+# tile-kernel shapes whose grid is small enough (at most 128 tiles, at least 1024 keys) that
+# the keys are split into ranges: ranges past a sequence's keys (empty), ranges above the causal
+# diagonal, an empty query sequence, key counts off the 64-key tile, more queries than keys
+SPLIT = {
+    "chunk": ([300, 77], [3000, 1100]),
+    "self": ([1500, 129], [1500, 129]),
+    "ragged": ([1, 257, 0], [2049, 4000, 700]),
+    "more_q": ([2000], [1030]),
+}
+
+
+@pytest.mark.parametrize("out_dtype", [BF16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("shape", list(SPLIT))
+def test_prefill_kernel_split_keys(shape, mask, d, out_dtype):
+    lq, lk = SPLIT[shape]
+    H = 2
+    n = fa.varlen_workspace_size(len(lq), H, max(lq), max(lk), d)
+    assert n > 0, "the shape should take the split path"
+    check(lq, lk, H, d, mask, out_dtype, seed=60 + d, label=f"split {shape} mask={mask} d={d} out={out_dtype} ({n} B)")
+
+
 def test_prefill_kernel_paired_launch():
     """Enough causal tiles (32 sequences x 64 heads x 3 tiles) that the launch pairs tiles
     (n-1-t, t) of each sequence; ragged lengths from 1 to 300, every row checked."""
@@ -151,7 +175,8 @@ def test_sequences_are_isolated(max_q_rows):
         assert torch.equal(a[1][:, s], b[1][:, s])
 
 
-@pytest.mark.parametrize("lq,lk", [([300, 41], [500, 800]), ([1, 1, 1, 1], [6000, 5, 9000, 300])])
+@pytest.mark.parametrize("lq,lk", [([300, 41], [500, 800]), ([1, 1, 1, 1], [6000, 5, 9000, 300]),
+                                   ([300, 41], [3000, 1100])])
 def test_bitwise_determinism_and_workspace_reuse(lq, lk):
     q, k, v, cu_q, cu_k = W.random_packed(lq, lk, 4, 64, BF16, seed=32)
     scale = W.scale_for(64)

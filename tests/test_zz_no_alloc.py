@@ -65,6 +65,8 @@ PAIRS = {
     "one_row": (([1] * 4, [8192] * 4, 16, 128), ([1] * 2, [3000, 700], 8, 128)),
     "four_rows": (([4, 3, 4], [5000, 4100, 9000], 8, 64), ([2, 4], [1500, 2600], 4, 64)),
     "decode_then_prefill": (([1, 1, 1], [4000, 0, 1200], 4, 128), ([30, 20], [700, 100], 2, 128)),
+    # prefill shapes whose keys are split into ranges (the split tile kernel and its merge)
+    "prefill_split": (([300, 77], [3000, 1100], 2, 128), ([200], [1500], 1, 128)),
 }
 
 
@@ -85,3 +87,22 @@ def test_noalloc_equals_workspace_entry_point_on_two_calls(pair, out_dtype):
                                                    causal=causal, align=align)
         res = PU.compare(o_na, l_na, O_ref, L_ref, out_dtype, label=label)
         print(f"[noalloc] {label}: {res}", flush=True)
+
+
+def test_noalloc_prefill_split_beyond_the_array_runs_unsplit():
+    """A prefill shape whose split keys need more workspace than the fixed array holds: the
+    allocation-free entry point runs the tiled kernel unsplit (no error, nothing allocated), and
+    its output matches the oracle; the workspace entry point splits."""
+    lq, lk, H, d = [3000], [3000], 4, 128
+    assert fa.varlen_workspace_size(len(lq), H, max(lq), max(lk), d) > fa.binding.scratch_bytes()
+    q, k, v, cu_q, cu_k = _inputs(lq, lk, H, d, seed=720)
+    for out_dtype in (BF16, torch.float32):
+        label = f"prefill beyond the array: lq={lq} H={H} d={d} out={out_dtype}"
+        print(f"[noalloc] {label}", flush=True)
+        o_na, l_na, o_ws, l_ws, fb, fa_ = _both(q, k, v, cu_q, cu_k, lq, lk, d, True, "bottom_right", out_dtype)
+        assert fb == fa_, f"{label}: free device memory changed by {fb - fa_} bytes"
+        O_ref, L_ref = oracle.attention_varlen_ref(q, k, v, cu_q.tolist(), cu_k.tolist(), W.scale_for(d),
+                                                   causal=True, align="bottom_right")
+        for name, (o, l) in (("noalloc", (o_na, l_na)), ("workspace", (o_ws, l_ws))):
+            res = PU.compare(o, l, O_ref, L_ref, out_dtype, label=f"{label} {name}")
+            print(f"[noalloc] {label} {name}: {res}", flush=True)
