@@ -14,9 +14,9 @@ resident in device memory.  Prints one JSON line:
              workload (seed-chosen query rows of every head), scaled to TFLOP/s.
 
 Packed variable-length workloads (--workload decode_c2kv | decode_c4kv | chunked_prefill |
-varlen_mix) time fa_fwd_varlen instead: decoding steps are bound by the K/V stream and are
-reported in GB/s against the HBM peak; packed prefill in TFLOP/s counting 4*d FLOP per visible
-(query, key) pair.
+varlen_mix | single_4k_d64 | single_8k_d128) time fa_fwd_varlen instead: decoding steps are
+bound by the K/V stream and are reported in GB/s against the HBM peak; packed prefill in
+TFLOP/s counting 4*d FLOP per visible (query, key) pair.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2] [--no-cpu-baseline]
        python bench.py --calibrate-copy      (a plain conversion copy of known size, for scaling
@@ -171,7 +171,8 @@ def bench_packed(args, w) -> int:
         "config": {
             "workload": f"{w.name}: {w.description}; {mask_name} mask; bf16 in, bf16 out, fp32 LSE",
             "sequences": len(w.lq), "H": w.H, "d": w.d, "tokens_q": Tq, "tokens_k": Tk,
-            "max_seqlen_q": mq, "max_seqlen_k": mk, "kernel": "decode (split keys + merge)" if decode else "tile",
+            "max_seqlen_q": mq, "max_seqlen_k": mk, "kernel": ("decode (split keys + merge)" if decode else
+                                                  "tile, keys split into ranges + merge" if nws else "tile"),
             "workspace_bytes": nws, "flop_per_step": flops, "compulsory_bytes_per_step": nbytes,
         },
         "roofline": {
@@ -180,7 +181,7 @@ def bench_packed(args, w) -> int:
             "kernel_avg_ms": round(avg_launch_s * 1e3, 5),
         },
     }
-    if decode and nws:
+    if nws:
         res["roofline"]["note"] = "HIP events bracket both kernels of a step (the key ranges and their merge)"
     if not args.no_cpu_baseline:
         import oracle
@@ -275,7 +276,8 @@ def main() -> int:
     ap.add_argument("--workload", default="c2",
                     help="c0..c4 (default c2, the roofline workload), a short-sequence HBM probe "
                          "bw<N>d<d> with N in 128/256/512 and d in 64/128, or a packed workload "
-                         "(decode_c2kv, decode_c4kv, chunked_prefill, varlen_mix)")
+                         "(decode_c2kv, decode_c4kv, chunked_prefill, varlen_mix, single_4k_d64, "
+                         "single_8k_d128)")
     ap.add_argument("--mask", type=int, default=None, help="override the workload's mask bits")
     ap.add_argument("--out-dtype", default=None, choices=[None, "bf16", "f32"])
     ap.add_argument("--variant", type=int, default=0)

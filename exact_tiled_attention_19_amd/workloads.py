@@ -203,6 +203,15 @@ PACKED = {
                                       seed=22, sample_seqs=1,
                                       description="the last 512 positions of four 8192-token sequences "
                                                   "(H=16, d=128), bottom-right causal"),
+    "single_4k_d64": PackedWorkload("single_4k_d64", 1, 64, (4096,), (4096,), False, "bottom_right", seed=24,
+                                    sample_seqs=1,
+                                    description="one 4096-token sequence, H=1, d=64, no mask (the c1 shape) through "
+                                                "the packed entry point, whose workspace lets the keys split across "
+                                                "workgroups"),
+    "single_8k_d128": PackedWorkload("single_8k_d128", 2, 128, (8192,), (8192,), True, "bottom_right", seed=25,
+                                     sample_seqs=1,
+                                     description="one 8192-token causal sequence, H=2, d=128, through the packed "
+                                                 "entry point"),
     "varlen_mix": PackedWorkload("varlen_mix", 16, 128, _MIX, _MIX, True, "bottom_right", seed=23, sample_seqs=2,
                                  description="16 packed causal sequences, lengths uniform on [256, 4096] "
                                              f"({sum(_MIX)} tokens, H=16, d=128)"),

@@ -130,7 +130,7 @@ def test_decode_workloads_full_size(name):
     check(list(w.lq), list(w.lk), w.H, w.d, "causal_br" if w.causal else "none", BF16, w.seed, f"workload {name}")
 
 
-@pytest.mark.parametrize("name", ["chunked_prefill", "varlen_mix"])
+@pytest.mark.parametrize("name", ["chunked_prefill", "varlen_mix", "single_4k_d64", "single_8k_d128"])
 def test_packed_workloads_full_size_sampled(name):
     """Full-size packed prefill: every sequence runs on the GPU; the first `sample_seqs`
     sequences are checked (chunked prefill: all their rows through the variable-length oracle;
