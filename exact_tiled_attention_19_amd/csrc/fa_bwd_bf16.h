@@ -18,8 +18,8 @@
 //                        dK^T += Q^T dS (MFMA, A read from LDS with the transpose read, B
 //                        straight from the S/dP accumulator registers).
 //   fa_bwd_dq_kernel     one workgroup per (batch, head, 128 query rows), 32 rows per wave;
-//                        Q^T and dO^T in VGPRs while 64-key tiles of K and V stream through
-//                        double-buffered LDS.
+//                        Q^T and dO^T in registers while 64-key tiles of K and V stream
+//                        global -> LDS directly (double-buffered, no register staging).
 //                        Per tile: S^T = K Q^T and dP^T = V dO^T; P^T and dS^T elementwise;
 //                        dQ^T += K^T dS^T.
 // In every 32x32 accumulator a lane owns one column (a key in dkdv, a query row in dq) and 16
@@ -94,6 +94,17 @@ __device__ __forceinline__ bf16x8 bwd_trfrag(const unsigned char* tile, int l32,
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
+// Waits until this wave's global -> LDS loads have completed (vmcnt(0)).
+__device__ __forceinline__ void bwd_wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Two 4 x 16 transpose reads at LDS addresses p0 and p1, joined into one A operand.
+__device__ __forceinline__ bf16x8 bwd_tr_pair(const unsigned char* p0, const unsigned char* p1) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0));
+    const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1));
+    return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
 // Copies rows [g0, g0 + ROWS) of a [N, D] bf16 matrix into a swizzled LDS tile (rows past N
 // are zero).  Split into fetch (global -> VGPRs, issued early) and stash (VGPRs -> LDS).
 template <int D, int ROWS>
@@ -116,6 +127,42 @@ struct TileStage {
             const int id = i * 256 + tid, row = id / CPR, ch = id % CPR;
             *(bf16x8*)(tile + bwd_lds_off<D>(row, ch)) = r[i];
         }
+    }
+};
+
+// 16 bytes per lane from a buffer resource straight into LDS (lane i's bytes land at lds + 16 i).
+// A plain device function: the builtin exists for the device only, and inside a template or
+// lambda the host pass would drop the kernels that use it.
+__device__ __forceinline__ void bwd_load_lds16(__amdgpu_buffer_rsrc_t rsrc, unsigned char* lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Rows [g0, g0 + ROWS) of a [N, D] bf16 matrix straight from global memory into the swizzled
+// LDS tile layout above, with buffer_load_dwordx4 ... lds (no register staging): each
+// instruction fills 1 KiB of LDS in lane order, so lane lam of piece r writes physical chunk
+// p = 64 r + lam (row p / CPR, chunk p % CPR) and fetches the logical chunk that the swizzle maps
+// there.  The buffer's byte range ends with row N - 1, so rows past it read as zeros.  The
+// loads complete asynchronously: wait for them (vmcnt) and a barrier before the tile is read.
+template <int D, int ROWS, int NW>
+struct TileDirect {
+    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    static constexpr int LPW = ROWS * D * 2 / 1024 / NW;  // 1 KiB pieces per wave
+    static_assert(LPW >= 1 && LPW * NW * 1024 == ROWS * D * 2, "tile must split into 1 KiB pieces per wave");
+    uint32_t off[LPW];
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int p = (i * NW + wave) * 64 + lane;
+            const int row = p / CPR, pch = p % CPR;
+            off[i] = row * (D * 2) + ((pch ^ bwd_swz<D>(row)) << 4);
+        }
+    }
+    __device__ __forceinline__ void load(unsigned char* tile, const uint16_t* m, int g0, int N, int wave) const {
+        const int64_t left = (int64_t)(N - g0) * (D * 2);
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(m + (int64_t)g0 * D), (short)0, left > 0 ? (int)(uint32_t)left : 0, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) bwd_load_lds16(rs, tile + (i * NW + wave) * 1024, off[i]);
     }
 };
 
@@ -388,19 +435,44 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
     const int nj = (kv_end + BN - 1) / BN;
     const uint16_t* kg = (const uint16_t*)a.k + base;
     const uint16_t* vg = (const uint16_t*)a.v + base;
-    TileStage<D, BN> sk, sv;
-    if (nj > 0) {
-        sk.fetch(kg, 0, N, tid);
-        sv.fetch(vg, 0, N, tid);
-        sk.stash(ks[0], tid);
-        sv.stash(vs[0], tid);
+    // K and V tiles go straight to LDS; tile j+1 is loaded into the buffers that tile j-1 left
+    // (every wave passed the barrier after reading them) while tile j is computed
+    TileDirect<D, BN, 4> ld;
+    ld.init(wave, lane);
+    // per-lane LDS byte offsets (the tile and block offsets are added as constants): whole-row
+    // operand of k-step c (row l32, chunk 2c + hh), and the two transpose reads of block db
+    // (rows vrow and vrow + 8 of the 16-row step, bwd_trfrag's addressing)
+    constexpr int ROWB = D * 2;
+    int roff[KC], toff0[NDB], toff1[NDB];
+#pragma unroll
+    for (int c = 0; c < KC; ++c) roff[c] = bwd_lds_off<D>(l32, 2 * c + hh);
+    {
+        const int vrow = 4 * hh + ((l32 & 15) >> 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+            const int chunk = 4 * db + ((l32 & 16) >> 3) + ((l32 & 3) >> 1);
+            toff0[db] = vrow * ROWB + ((chunk ^ bwd_swz<D>(vrow)) << 4) + (l32 & 1) * 8;
+            toff1[db] = (vrow + 8) * ROWB + ((chunk ^ bwd_swz<D>(vrow + 8)) << 4) + (l32 & 1) * 8;
+        }
     }
+    auto rfrag = [&](const unsigned char* t, int kb, int c) __attribute__((always_inline)) -> bf16x8 {
+        return *(const bf16x8*)(t + 32 * kb * ROWB + roff[c]);
+    };
+    auto tfrag = [&](const unsigned char* t, int pc, int db) __attribute__((always_inline)) -> bf16x8 {
+        return bwd_tr_pair(t + 16 * pc * ROWB + toff0[db], t + 16 * pc * ROWB + toff1[db]);
+    };
+    if (nj > 0) {
+        ld.load(ks[0], kg, 0, N, wave);
+        ld.load(vs[0], vg, 0, N, wave);
+    }
+    bwd_wait_loads();
     __syncthreads();
-    for (int j = 0; j < nj; ++j) {
-        const int cur = j & 1;
+    // One tile; the loop below runs tiles in pairs with literal buffer parities, so after inlining
+    // every LDS address is a per-lane register plus an immediate offset.
+    auto tile = [&](const int cur, int j) __attribute__((always_inline)) {
         if (j + 1 < nj) {
-            sk.fetch(kg, (j + 1) * BN, N, tid);
-            sv.fetch(vg, (j + 1) * BN, N, tid);
+            ld.load(ks[cur ^ 1], kg, (j + 1) * BN, N, wave);
+            ld.load(vs[cur ^ 1], vg, (j + 1) * BN, N, wave);
         }
         const unsigned char* kt_ = ks[cur];
         const unsigned char* vt_ = vs[cur];
@@ -409,21 +481,33 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
         // diagonal) or past the valid length (and past N)
         const bool masked = (CAUSAL && j0 + BN - 1 > qw0) || j0 + BN > Lk;
         // S^T = K Q^T, dP^T = V dO^T per 32-key block: lane (row, hh) holds keys
-        // 32kb + 8(r/4) + 4hh + r%4 (inside each arm of the mask branch, as in the dK/dV kernel)
+        // 32kb + 8(r/4) + 4hh + r%4 (inside each arm of the mask branch, as in the dK/dV kernel).
+        // One 32-key block at a time (its S^T, dP^T, dS^T and dQ^T products), so that only one
+        // block's scores are live.  Issue order: one slot per k-step with its two MFMAs, the LDS
+        // operands read two slots ahead, slots kept apart by sched_barrier, so at most three
+        // slots' fragments are live and every read has two MFMAs of time to return.
         f32x16 s[NKB], dp[NKB];
-        auto sdp = [&]() __attribute__((always_inline)) {
+        auto sdp = [&](int kb) __attribute__((always_inline)) {
+            s[kb] = dp[kb] = f32x16{};
+            bf16x8 kf0 = rfrag(kt_, kb, 0), vf0 = rfrag(vt_, kb, 0);
+            bf16x8 kf1 = rfrag(kt_, kb, 1), vf1 = rfrag(vt_, kb, 1);
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) {
-                s[kb] = dp[kb] = f32x16{};
-#pragma unroll
-                for (int c = 0; c < KC; ++c) {
-                    s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(kt_, 32 * kb, l32, hh, c), qt[c], s[kb], 0, 0, 0);
-                    dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(vt_, 32 * kb, l32, hh, c), dot[c], dp[kb], 0, 0, 0);
+            for (int c = 0; c < KC; ++c) {
+                bf16x8 kf2 = kf1, vf2 = vf1;
+                if (c + 2 < KC) {
+                    kf2 = rfrag(kt_, kb, c + 2);
+                    vf2 = rfrag(vt_, kb, c + 2);
                 }
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qt[c], s[kb], 0, 0, 0);
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, dot[c], dp[kb], 0, 0, 0);
+                kf0 = kf1;
+                kf1 = kf2;
+                vf0 = vf1;
+                vf1 = vf2;
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
-        // dS^T = P^T (dP^T - D) on visible pairs, packed as the B operand of dQ^T += K^T dS^T;
-        // block 1's products overlap block 0's vector work
+        // dS^T = P^T (dP^T - D) on visible pairs, packed as the B operand of dQ^T += K^T dS^T
         auto block = [&](int kb, auto masked_c) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_c)::value;
             u32x4 dsh[2];
@@ -449,28 +533,43 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
                 }
                 dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
             }
+            // dQ^T += K^T dS^T, the transpose-read operands two products ahead
+            constexpr int NP = 2 * NDB;
+            bf16x8 f0 = tfrag(kt_, 2 * kb, 0);
+            bf16x8 f1 = tfrag(kt_, 2 * kb + 1 / NDB, 1 % NDB);
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc)
-#pragma unroll
-                for (int db = 0; db < NDB; ++db)
-                    dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(kt_, l32, hh, 2 * kb + pc, db),
-                                                                     __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
+            for (int i = 0; i < NP; ++i) {
+                const int pc = i / NDB, db = i % NDB;
+                bf16x8 f2 = f1;
+                if (i + 2 < NP) f2 = tfrag(kt_, 2 * kb + (i + 2) / NDB, (i + 2) % NDB);
+                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
+                f0 = f1;
+                f1 = f2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
         if (masked) {
-            sdp();
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) block(kb, std::true_type{});
+            for (int kb = 0; kb < NKB; ++kb) {
+                sdp(kb);
+                block(kb, std::true_type{});
+            }
         } else {
-            sdp();
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb) block(kb, std::false_type{});
+            for (int kb = 0; kb < NKB; ++kb) {
+                sdp(kb);
+                block(kb, std::false_type{});
+            }
         }
-        if (j + 1 < nj) {
-            sk.stash(ks[cur ^ 1], tid);
-            sv.stash(vs[cur ^ 1], tid);
-        }
+        bwd_wait_loads();   // tile j+1 is in LDS
         __syncthreads();
+    };
+    int j = 0;
+    for (; j + 2 <= nj; j += 2) {
+        tile(0, j);
+        tile(1, j + 1);
     }
+    if (j < nj) tile(0, j);
     if (row_ok) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
