@@ -291,14 +291,39 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
         // 8(r/4) + 4hh + r%4.  Computed inside each arm of the mask branch below, so that one
         // basic block holds the whole tile and half 0's vector work can overlap half 1's MFMAs.
         f32x16 s[NH], dp[NH];
+        // Issue order: one slot per k-step with its two MFMAs, the LDS operands read two slots
+        // ahead, slots kept apart by sched_barrier, so every read has four MFMAs of time to
+        // return.  The dropout instantiations, whose mask bits take more registers, keep the
+        // compiler's own order (the pinned one would spill there).
         auto sdp = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
                 s[h] = dp[h] = f32x16{};
+                if constexpr (DROP) {
+#pragma unroll
+                    for (int c = 0; c < KC; ++c) {
+                        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c), kt[c], s[h], 0, 0, 0);
+                        dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c), vt[c], dp[h], 0, 0, 0);
+                    }
+                    continue;
+                }
+                // the LDS operands two slots (four MFMAs) ahead
+                bf16x8 fq0 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 0), fd0 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 0);
+                bf16x8 fq1 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 1), fd1 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 1);
 #pragma unroll
                 for (int c = 0; c < KC; ++c) {
-                    s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c), kt[c], s[h], 0, 0, 0);
-                    dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c), vt[c], dp[h], 0, 0, 0);
+                    bf16x8 fq2 = fq1, fd2 = fd1;
+                    if (c + 2 < KC) {
+                        fq2 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c + 2);
+                        fd2 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c + 2);
+                    }
+                    s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, kt[c], s[h], 0, 0, 0);
+                    dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, vt[c], dp[h], 0, 0, 0);
+                    fq0 = fq1;
+                    fd0 = fd1;
+                    fq1 = fq2;
+                    fd1 = fd2;
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
         };
@@ -339,15 +364,39 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
                 dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
                 dsh[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(ds[2], ds[3]);
             }
+            if constexpr (DROP) {
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc)
+                for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(dt_, l32, hh, 2 * h + pc, db),
-                                                                     __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
-                    dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(qt_, l32, hh, 2 * h + pc, db),
-                                                                     __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                    for (int db = 0; db < NDB; ++db) {
+                        dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(dt_, l32, hh, 2 * h + pc, db),
+                                                                         __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
+                        dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(qt_, l32, hh, 2 * h + pc, db),
+                                                                         __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                    }
+                return;
+            }
+            // the transpose-read operands two slots (four MFMAs) ahead
+            constexpr int NP = 2 * NDB;
+            bf16x8 fd0 = bwd_trfrag<D>(dt_, l32, hh, 2 * h, 0), fq0 = bwd_trfrag<D>(qt_, l32, hh, 2 * h, 0);
+            bf16x8 fd1 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
+            bf16x8 fq1 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int pc = i / NDB, db = i % NDB;
+                bf16x8 fd2 = fd1, fq2 = fq1;
+                if (i + 2 < NP) {
+                    fd2 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
+                    fq2 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
                 }
+                dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
+                dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                fd0 = fd1;
+                fq0 = fq1;
+                fd1 = fd2;
+                fq1 = fq2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
         };
         if (masked) {
             sdp();
