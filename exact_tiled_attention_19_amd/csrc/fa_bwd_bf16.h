@@ -398,7 +398,89 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if (masked) {
+        // Two halves without dropout: the tile as one sequence of slots in which each half's
+        // vector work rides on the other half's MFMAs -- half 0's P and dS on the S/dP products
+        // of half 1, half 1's on the dV/dK products of half 0 -- instead of running between them.
+        auto sdp_h = [&](int h, auto hook) __attribute__((always_inline)) {
+            s[h] = dp[h] = f32x16{};
+            bf16x8 fq0 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 0), fd0 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 0);
+            bf16x8 fq1 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 1), fd1 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 1);
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                bf16x8 fq2 = fq1, fd2 = fd1;
+                if (c + 2 < KC) {
+                    fq2 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c + 2);
+                    fd2 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c + 2);
+                }
+                s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, kt[c], s[h], 0, 0, 0);
+                dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, vt[c], dp[h], 0, 0, 0);
+                hook(c);
+                fq0 = fq1;
+                fd0 = fd1;
+                fq1 = fq2;
+                fd1 = fd2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto prod_h = [&](int h, const u32x4 (&ph)[2], const u32x4 (&dsh)[2], auto hook) __attribute__((always_inline)) {
+            constexpr int NP = 2 * NDB;
+            bf16x8 fd0 = bwd_trfrag<D>(dt_, l32, hh, 2 * h, 0), fq0 = bwd_trfrag<D>(qt_, l32, hh, 2 * h, 0);
+            bf16x8 fd1 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
+            bf16x8 fq1 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int pc = i / NDB, db = i % NDB;
+                bf16x8 fd2 = fd1, fq2 = fq1;
+                if (i + 2 < NP) {
+                    fd2 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
+                    fq2 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
+                }
+                dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
+                dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                hook(i);
+                fd0 = fd1;
+                fq0 = fq1;
+                fd1 = fd2;
+                fq1 = fq2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // P and dS of rows 4rq .. 4rq+3 of half h's 32-row block (lane rows 8rq + 4hh ..)
+        auto pds = [&](int h, int rq, auto masked_c, u32x4 (&ph)[2], u32x4 (&dsh)[2]) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            const int r = 4 * rq;
+            const int rr = 32 * h + 8 * rq + 4 * hh;
+            const f32x4 l4 = *(const f32x4*)(ls + rr);
+            const f32x4 d4 = *(const f32x4*)(dd + rr);
+            float p[4], ds[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                float e = fast_exp2(fmaf(s[h][r + u], a.scale_log2, -l4[u]));
+                if constexpr (MASKED) {
+                    const int g = r0 + rr + u;
+                    const bool ok = g < N && key < Lk && (!CAUSAL || key <= g);
+                    e = ok ? e : 0.f;
+                }
+                p[u] = e;
+                ds[u] = e * (dp[h][r + u] - d4[u]);
+            }
+            ph[r / 8][(r % 8) / 2] = pack_bf16x2(p[0], p[1]);
+            ph[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(p[2], p[3]);
+            dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
+            dsh[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(ds[2], ds[3]);
+        };
+        auto piped = [&](auto masked_c) __attribute__((always_inline)) {
+            u32x4 ph0[2], dsh0[2], ph1[2], dsh1[2];
+            sdp_h(0, [&](int) {});
+            sdp_h(1, [&](int c) { if (c & 1) pds(0, c >> 1, masked_c, ph0, dsh0); });
+            prod_h(0, ph0, dsh0, [&](int i) { if (i & 1) pds(1, i >> 1, masked_c, ph1, dsh1); });
+            prod_h(1, ph1, dsh1, [&](int) {});
+        };
+        constexpr bool PIPED = !DROP && NH == 2 && KC == 8 && NDB == 4;
+        if constexpr (PIPED) {
+            if (masked) piped(std::true_type{});
+            else piped(std::false_type{});
+        } else if (masked) {
             sdp();
 #pragma unroll
             for (int h = 0; h < NH; ++h) half(h, std::true_type{});
