@@ -679,7 +679,81 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
-        if (masked) {
+        // Without dropout the two key blocks run as one sequence of slots in which each block's
+        // dS^T work rides on the other block's MFMAs: block 0's on the S^T/dP^T products of
+        // block 1, block 1's on the dQ^T products of block 0.
+        auto sdp_k = [&](int kb, auto hook) __attribute__((always_inline)) {
+            s[kb] = dp[kb] = f32x16{};
+            bf16x8 kf0 = rfrag(kt_, kb, 0), vf0 = rfrag(vt_, kb, 0);
+            bf16x8 kf1 = rfrag(kt_, kb, 1), vf1 = rfrag(vt_, kb, 1);
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                bf16x8 kf2 = kf1, vf2 = vf1;
+                if (c + 2 < KC) {
+                    kf2 = rfrag(kt_, kb, c + 2);
+                    vf2 = rfrag(vt_, kb, c + 2);
+                }
+                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qt[c], s[kb], 0, 0, 0);
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, dot[c], dp[kb], 0, 0, 0);
+                hook(c);
+                kf0 = kf1;
+                kf1 = kf2;
+                vf0 = vf1;
+                vf1 = vf2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        // dS^T of keys 8(it/4) + 4hh + (2it)%8 .. +1 of block kb (registers 2it, 2it + 1)
+        auto ds_pair = [&](int kb, int it, auto masked_c, u32x4 (&dsh)[2]) __attribute__((always_inline)) {
+            constexpr bool MASKED = decltype(masked_c)::value;
+            const int r = 2 * it;
+            float ds[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                float e = fast_exp2(fmaf(s[kb][r + u], a.scale_log2, -lse2));
+                if constexpr (MASKED) {
+                    const int key = j0 + 32 * kb + 8 * ((r + u) >> 2) + 4 * hh + ((r + u) & 3);
+                    const bool ok = key < Lk && (!CAUSAL || key <= row);
+                    e = ok ? e : 0.f;
+                }
+                ds[u] = e * (dp[kb][r + u] - dl);
+            }
+            dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
+        };
+        auto prod_k = [&](int kb, const u32x4 (&dsh)[2], auto hook) __attribute__((always_inline)) {
+            constexpr int NP = 2 * NDB;
+            bf16x8 f0 = tfrag(kt_, 2 * kb, 0);
+            bf16x8 f1 = tfrag(kt_, 2 * kb + 1 / NDB, 1 % NDB);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int pc = i / NDB, db = i % NDB;
+                bf16x8 f2 = f1;
+                if (i + 2 < NP) f2 = tfrag(kt_, 2 * kb + (i + 2) / NDB, (i + 2) % NDB);
+                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
+                hook(i);
+                f0 = f1;
+                f1 = f2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto piped = [&](auto masked_c) __attribute__((always_inline)) {
+            constexpr int NP = 2 * NDB;
+            u32x4 dsh0[2], dsh1[2];
+            sdp_k(0, [&](int) {});
+            sdp_k(1, [&](int c) {
+#pragma unroll
+                for (int it = c * 8 / KC; it < (c + 1) * 8 / KC; ++it) ds_pair(0, it, masked_c, dsh0);
+            });
+            prod_k(0, dsh0, [&](int i) {
+#pragma unroll
+                for (int it = i * 8 / NP; it < (i + 1) * 8 / NP; ++it) ds_pair(1, it, masked_c, dsh1);
+            });
+            prod_k(1, dsh1, [&](int) {});
+        };
+        if constexpr (!DROP && NKB == 2) {
+            if (masked) piped(std::true_type{});
+            else piped(std::false_type{});
+        } else if (masked) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 sdp(kb);
