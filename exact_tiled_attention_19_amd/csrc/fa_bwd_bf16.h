@@ -291,39 +291,67 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
         // 8(r/4) + 4hh + r%4.  Computed inside each arm of the mask branch below, so that one
         // basic block holds the whole tile and half 0's vector work can overlap half 1's MFMAs.
         f32x16 s[NH], dp[NH];
-        // Issue order: one slot per k-step with its two MFMAs, the LDS operands read two slots
-        // ahead, slots kept apart by sched_barrier, so every read has four MFMAs of time to
-        // return.  The dropout instantiations, whose mask bits take more registers, keep the
-        // compiler's own order (the pinned one would spill there).
+        // Issue order (without dropout): one slot per k-step with its MFMAs, the LDS operands
+        // read two slots ahead, slots kept apart by sched_barrier, so every read has four MFMAs
+        // of time to return; hook(slot) places vector work beside them.  The dropout
+        // instantiations, whose mask bits take more registers, keep the compiler's own order
+        // (the pinned one would spill there).
+        auto sdp_h = [&](int h, auto hook) __attribute__((always_inline)) {
+            s[h] = dp[h] = f32x16{};
+            bf16x8 fq0 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 0), fd0 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 0);
+            bf16x8 fq1 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 1), fd1 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 1);
+#pragma unroll
+            for (int c = 0; c < KC; ++c) {
+                bf16x8 fq2 = fq1, fd2 = fd1;
+                if (c + 2 < KC) {
+                    fq2 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c + 2);
+                    fd2 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c + 2);
+                }
+                s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, kt[c], s[h], 0, 0, 0);
+                dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, vt[c], dp[h], 0, 0, 0);
+                hook(c);
+                fq0 = fq1;
+                fd0 = fd1;
+                fq1 = fq2;
+                fd1 = fd2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto prod_h = [&](int h, const u32x4 (&ph)[2], const u32x4 (&dsh)[2], auto hook) __attribute__((always_inline)) {
+            constexpr int NP = 2 * NDB;
+            bf16x8 fd0 = bwd_trfrag<D>(dt_, l32, hh, 2 * h, 0), fq0 = bwd_trfrag<D>(qt_, l32, hh, 2 * h, 0);
+            bf16x8 fd1 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
+            bf16x8 fq1 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int pc = i / NDB, db = i % NDB;
+                bf16x8 fd2 = fd1, fq2 = fq1;
+                if (i + 2 < NP) {
+                    fd2 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
+                    fq2 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
+                }
+                dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
+                dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
+                hook(i);
+                fd0 = fd1;
+                fq0 = fq1;
+                fd1 = fd2;
+                fq1 = fq2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
         auto sdp = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-                s[h] = dp[h] = f32x16{};
                 if constexpr (DROP) {
+                    s[h] = dp[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < KC; ++c) {
                         s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c), kt[c], s[h], 0, 0, 0);
                         dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c), vt[c], dp[h], 0, 0, 0);
                     }
-                    continue;
-                }
-                // the LDS operands two slots (four MFMAs) ahead
-                bf16x8 fq0 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 0), fd0 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 0);
-                bf16x8 fq1 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 1), fd1 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 1);
-#pragma unroll
-                for (int c = 0; c < KC; ++c) {
-                    bf16x8 fq2 = fq1, fd2 = fd1;
-                    if (c + 2 < KC) {
-                        fq2 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c + 2);
-                        fd2 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c + 2);
-                    }
-                    s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, kt[c], s[h], 0, 0, 0);
-                    dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, vt[c], dp[h], 0, 0, 0);
-                    fq0 = fq1;
-                    fd0 = fd1;
-                    fq1 = fq2;
-                    fd1 = fd2;
-                    __builtin_amdgcn_sched_barrier(0);
+                } else {
+                    sdp_h(h, [](int) {});
                 }
             }
         };
@@ -374,77 +402,13 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
                         dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_trfrag<D>(qt_, l32, hh, 2 * h + pc, db),
                                                                          __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
                     }
-                return;
-            }
-            // the transpose-read operands two slots (four MFMAs) ahead
-            constexpr int NP = 2 * NDB;
-            bf16x8 fd0 = bwd_trfrag<D>(dt_, l32, hh, 2 * h, 0), fq0 = bwd_trfrag<D>(qt_, l32, hh, 2 * h, 0);
-            bf16x8 fd1 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
-            bf16x8 fq1 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int pc = i / NDB, db = i % NDB;
-                bf16x8 fd2 = fd1, fq2 = fq1;
-                if (i + 2 < NP) {
-                    fd2 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
-                    fq2 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
-                }
-                dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
-                dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
-                fd0 = fd1;
-                fq0 = fq1;
-                fd1 = fd2;
-                fq1 = fq2;
-                __builtin_amdgcn_sched_barrier(0);
+            } else {
+                prod_h(h, ph, dsh, [](int) {});
             }
         };
         // Two halves without dropout: the tile as one sequence of slots in which each half's
         // vector work rides on the other half's MFMAs -- half 0's P and dS on the S/dP products
         // of half 1, half 1's on the dV/dK products of half 0 -- instead of running between them.
-        auto sdp_h = [&](int h, auto hook) __attribute__((always_inline)) {
-            s[h] = dp[h] = f32x16{};
-            bf16x8 fq0 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 0), fd0 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 0);
-            bf16x8 fq1 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, 1), fd1 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, 1);
-#pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                bf16x8 fq2 = fq1, fd2 = fd1;
-                if (c + 2 < KC) {
-                    fq2 = bwd_rowfrag<D>(qt_, 32 * h, l32, hh, c + 2);
-                    fd2 = bwd_rowfrag<D>(dt_, 32 * h, l32, hh, c + 2);
-                }
-                s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, kt[c], s[h], 0, 0, 0);
-                dp[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, vt[c], dp[h], 0, 0, 0);
-                hook(c);
-                fq0 = fq1;
-                fd0 = fd1;
-                fq1 = fq2;
-                fd1 = fd2;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        auto prod_h = [&](int h, const u32x4 (&ph)[2], const u32x4 (&dsh)[2], auto hook) __attribute__((always_inline)) {
-            constexpr int NP = 2 * NDB;
-            bf16x8 fd0 = bwd_trfrag<D>(dt_, l32, hh, 2 * h, 0), fq0 = bwd_trfrag<D>(qt_, l32, hh, 2 * h, 0);
-            bf16x8 fd1 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
-            bf16x8 fq1 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + 1 / NDB, 1 % NDB);
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int pc = i / NDB, db = i % NDB;
-                bf16x8 fd2 = fd1, fq2 = fq1;
-                if (i + 2 < NP) {
-                    fd2 = bwd_trfrag<D>(dt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
-                    fq2 = bwd_trfrag<D>(qt_, l32, hh, 2 * h + (i + 2) / NDB, (i + 2) % NDB);
-                }
-                dvt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd0, __builtin_bit_cast(bf16x8, ph[pc]), dvt[db], 0, 0, 0);
-                dkt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq0, __builtin_bit_cast(bf16x8, dsh[pc]), dkt[db], 0, 0, 0);
-                hook(i);
-                fd0 = fd1;
-                fq0 = fq1;
-                fd1 = fd2;
-                fq1 = fq2;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
         // P and dS of rows 4rq .. 4rq+3 of half h's 32-row block (lane rows 8rq + 4hh ..)
         auto pds = [&](int h, int rq, auto masked_c, u32x4 (&ph)[2], u32x4 (&dsh)[2]) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_c)::value;
@@ -618,7 +582,7 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
         // operands read two slots ahead, slots kept apart by sched_barrier, so at most three
         // slots' fragments are live and every read has two MFMAs of time to return.
         f32x16 s[NKB], dp[NKB];
-        auto sdp = [&](int kb) __attribute__((always_inline)) {
+        auto sdp_k = [&](int kb, auto hook) __attribute__((always_inline)) {
             s[kb] = dp[kb] = f32x16{};
             bf16x8 kf0 = rfrag(kt_, kb, 0), vf0 = rfrag(vt_, kb, 0);
             bf16x8 kf1 = rfrag(kt_, kb, 1), vf1 = rfrag(vt_, kb, 1);
@@ -631,6 +595,7 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
                 }
                 s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qt[c], s[kb], 0, 0, 0);
                 dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, dot[c], dp[kb], 0, 0, 0);
+                hook(c);
                 kf0 = kf1;
                 kf1 = kf2;
                 vf0 = vf1;
@@ -638,6 +603,23 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
                 __builtin_amdgcn_sched_barrier(0);
             }
         };
+        auto prod_k = [&](int kb, const u32x4 (&dsh)[2], auto hook) __attribute__((always_inline)) {
+            constexpr int NP = 2 * NDB;
+            bf16x8 f0 = tfrag(kt_, 2 * kb, 0);
+            bf16x8 f1 = tfrag(kt_, 2 * kb + 1 / NDB, 1 % NDB);
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+                const int pc = i / NDB, db = i % NDB;
+                bf16x8 f2 = f1;
+                if (i + 2 < NP) f2 = tfrag(kt_, 2 * kb + (i + 2) / NDB, (i + 2) % NDB);
+                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
+                hook(i);
+                f0 = f1;
+                f1 = f2;
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        auto sdp = [&](int kb) __attribute__((always_inline)) { sdp_k(kb, [](int) {}); };
         // dS^T = P^T (dP^T - D) on visible pairs, packed as the B operand of dQ^T += K^T dS^T
         auto block = [&](int kb, auto masked_c) __attribute__((always_inline)) {
             constexpr bool MASKED = decltype(masked_c)::value;
@@ -664,44 +646,7 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
                 }
                 dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
             }
-            // dQ^T += K^T dS^T, the transpose-read operands two products ahead
-            constexpr int NP = 2 * NDB;
-            bf16x8 f0 = tfrag(kt_, 2 * kb, 0);
-            bf16x8 f1 = tfrag(kt_, 2 * kb + 1 / NDB, 1 % NDB);
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int pc = i / NDB, db = i % NDB;
-                bf16x8 f2 = f1;
-                if (i + 2 < NP) f2 = tfrag(kt_, 2 * kb + (i + 2) / NDB, (i + 2) % NDB);
-                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
-                f0 = f1;
-                f1 = f2;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
-        // Without dropout the two key blocks run as one sequence of slots in which each block's
-        // dS^T work rides on the other block's MFMAs: block 0's on the S^T/dP^T products of
-        // block 1, block 1's on the dQ^T products of block 0.
-        auto sdp_k = [&](int kb, auto hook) __attribute__((always_inline)) {
-            s[kb] = dp[kb] = f32x16{};
-            bf16x8 kf0 = rfrag(kt_, kb, 0), vf0 = rfrag(vt_, kb, 0);
-            bf16x8 kf1 = rfrag(kt_, kb, 1), vf1 = rfrag(vt_, kb, 1);
-#pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                bf16x8 kf2 = kf1, vf2 = vf1;
-                if (c + 2 < KC) {
-                    kf2 = rfrag(kt_, kb, c + 2);
-                    vf2 = rfrag(vt_, kb, c + 2);
-                }
-                s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf0, qt[c], s[kb], 0, 0, 0);
-                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf0, dot[c], dp[kb], 0, 0, 0);
-                hook(c);
-                kf0 = kf1;
-                kf1 = kf2;
-                vf0 = vf1;
-                vf1 = vf2;
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            prod_k(kb, dsh, [](int) {});
         };
         // dS^T of keys 8(it/4) + 4hh + (2it)%8 .. +1 of block kb (registers 2it, 2it + 1)
         auto ds_pair = [&](int kb, int it, auto masked_c, u32x4 (&dsh)[2]) __attribute__((always_inline)) {
@@ -720,22 +665,9 @@ __global__ void __launch_bounds__(256, D == 128 ? 1 : 2) fa_bwd_dq_kernel(BwdArg
             }
             dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
         };
-        auto prod_k = [&](int kb, const u32x4 (&dsh)[2], auto hook) __attribute__((always_inline)) {
-            constexpr int NP = 2 * NDB;
-            bf16x8 f0 = tfrag(kt_, 2 * kb, 0);
-            bf16x8 f1 = tfrag(kt_, 2 * kb + 1 / NDB, 1 % NDB);
-#pragma unroll
-            for (int i = 0; i < NP; ++i) {
-                const int pc = i / NDB, db = i % NDB;
-                bf16x8 f2 = f1;
-                if (i + 2 < NP) f2 = tfrag(kt_, 2 * kb + (i + 2) / NDB, (i + 2) % NDB);
-                dqt[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0, __builtin_bit_cast(bf16x8, dsh[pc]), dqt[db], 0, 0, 0);
-                hook(i);
-                f0 = f1;
-                f1 = f2;
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        };
+        // Without dropout the two key blocks run as one sequence of slots in which each block's
+        // dS^T work rides on the other block's MFMAs: block 0's on the S^T/dP^T products of
+        // block 1, block 1's on the dQ^T products of block 0.
         auto piped = [&](auto masked_c) __attribute__((always_inline)) {
             constexpr int NP = 2 * NDB;
             u32x4 dsh0[2], dsh1[2];
