@@ -12,8 +12,9 @@
 // Three kernels, all on one stream, none with atomics (the result is run-to-run identical):
 //   fa_bwd_delta_kernel  D_i = dO_i . O_i for every row, into the caller's float32 workspace.
 //   fa_bwd_dkdv_kernel   one workgroup per (batch, head, 128 keys), 32 keys per wave; the
-//                        wave's K^T and V^T stay in VGPRs while 64-row tiles of Q and dO stream
-//                        through double-buffered LDS (one barrier per tile).  Per tile: S = Q K^T and dP = dO V^T (MFMA, A from LDS,
+//                        wave's K^T and V^T stay in VGPRs while 64- or 32-row tiles of Q and dO
+//                        stream global -> LDS directly (double-buffered, one barrier per tile).
+//                        Per tile: S = Q K^T and dP = dO V^T (MFMA, A from LDS,
 //                        B from VGPRs); P and dS elementwise; dV^T += dO^T P and
 //                        dK^T += Q^T dS (MFMA, A read from LDS with the transpose read, B
 //                        straight from the S/dP accumulator registers).
@@ -105,31 +106,6 @@ __device__ __forceinline__ bf16x8 bwd_tr_pair(const unsigned char* p0, const uns
     return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// Copies rows [g0, g0 + ROWS) of a [N, D] bf16 matrix into a swizzled LDS tile (rows past N
-// are zero).  Split into fetch (global -> VGPRs, issued early) and stash (VGPRs -> LDS).
-template <int D, int ROWS>
-struct TileStage {
-    static constexpr int CPR = D / 8;
-    static constexpr int PER_THREAD = ROWS * CPR / 256;
-    static_assert(PER_THREAD * 256 == ROWS * CPR, "tile must split evenly over 256 threads");
-    bf16x8 r[PER_THREAD];
-    __device__ __forceinline__ void fetch(const uint16_t* m, int g0, int N, int tid) {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int id = i * 256 + tid, row = id / CPR, ch = id % CPR;
-            const int g = g0 + row;
-            r[i] = g < N ? *(const bf16x8*)(m + (int64_t)g * D + ch * 8) : bf16x8{};
-        }
-    }
-    __device__ __forceinline__ void stash(unsigned char* tile, int tid) const {
-#pragma unroll
-        for (int i = 0; i < PER_THREAD; ++i) {
-            const int id = i * 256 + tid, row = id / CPR, ch = id % CPR;
-            *(bf16x8*)(tile + bwd_lds_off<D>(row, ch)) = r[i];
-        }
-    }
-};
-
 // 16 bytes per lane from a buffer resource straight into LDS (lane i's bytes land at lds + 16 i).
 // A plain device function: the builtin exists for the device only, and inside a template or
 // lambda the host pass would drop the kernels that use it.
@@ -187,16 +163,16 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
 }
 
 // Query rows per dK/dV tile.  d = 64: 32-row tiles keep two workgroups per CU.  d = 128 runs
-// one workgroup per CU; under the causal mask it takes 64-row tiles (two 32-row halves, so one
-// half's vector work can overlap the other's MFMAs), which in the unmasked variant would not
-// fit the register file.
-template <int D, bool CAUSAL>
-constexpr int bwd_bq() { return D == 128 && CAUSAL ? 64 : 32; }
+// one workgroup per CU with 64-row tiles (two 32-row halves, so that each half's vector work
+// rides on the other half's MFMAs); with dropout, whose mask bits take more registers, 32-row
+// tiles, which fit without spilling.
+template <int D, bool DROP>
+constexpr int bwd_bq() { return D == 128 && !DROP ? 64 : 32; }
 
 template <int D, bool CAUSAL, bool PAD, bool DROP = false>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int BK = 128;        // keys per workgroup (32 per wave)
-    constexpr int BQ = bwd_bq<D, CAUSAL>();  // query rows per tile, handled as 32-row halves
+    constexpr int BQ = bwd_bq<D, DROP>();  // query rows per tile, handled as 32-row halves
     constexpr int NH = BQ / 32;
     constexpr int KC = D / 16;     // k-steps over d
     constexpr int NDB = D / 32;    // 32-wide blocks of d
@@ -251,11 +227,16 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
     const uint16_t* dog = (const uint16_t*)a.dout + base;
     const float* lse_g = a.lse + (int64_t)bh * N;
     const float* dl_g = a.delta + (int64_t)bh * N;
-    TileStage<D, BQ> sq, sdo;
+    // Q and dO tiles go global -> LDS directly into the buffers that tile t-1 left (every wave
+    // passed the barrier after reading them) while tile t is computed; the rows' LSE and D
+    // values take a register round trip.  The buffers are numbered from t_begin, so the tile
+    // loop below runs in pairs with literal parities and the LDS offsets are immediates.
+    TileDirect<D, BQ, 4> ld;
+    ld.init(wave, lane);
     float plse = 0.f, pdl = 0.f;
-    auto fetch = [&](int t) __attribute__((always_inline)) {
-        sq.fetch(qg, t * BQ, N, tid);
-        sdo.fetch(dog, t * BQ, N, tid);
+    auto fetch = [&](int t, int buf) __attribute__((always_inline)) {
+        ld.load(qs[buf], qg, t * BQ, N, wave);
+        ld.load(dos[buf], dog, t * BQ, N, wave);
         if (tid < BQ) {
             const int g = t * BQ + tid;
             plse = g < N ? lse_g[g] * kLog2e : 0.f;
@@ -263,21 +244,19 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
         }
     };
     auto stash = [&](int buf) __attribute__((always_inline)) {
-        sq.stash(qs[buf], tid);
-        sdo.stash(dos[buf], tid);
         if (tid < BQ) {
             lse2s[buf][tid] = plse;
             dls[buf][tid] = pdl;
         }
     };
     if (t_begin < nt) {
-        fetch(t_begin);
-        stash(t_begin & 1);
+        fetch(t_begin, 0);
+        bwd_wait_loads();
+        stash(0);
     }
     __syncthreads();
-    for (int t = t_begin; t < nt; ++t) {
-        const int cur = t & 1;
-        if (t + 1 < nt) fetch(t + 1);            // global loads overlap this tile's work
+    auto tile = [&](const int cur, int t) __attribute__((always_inline)) {
+        if (t + 1 < nt) fetch(t + 1, cur ^ 1);   // global loads overlap this tile's work
         const unsigned char* qt_ = qs[cur];
         const unsigned char* dt_ = dos[cur];
         const float* ls = lse2s[cur];
@@ -453,9 +432,16 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
 #pragma unroll
             for (int h = 0; h < NH; ++h) half(h, std::false_type{});
         }
-        if (t + 1 < nt) stash((t + 1) & 1);
+        bwd_wait_loads();                        // tile t+1 is in LDS
+        if (t + 1 < nt) stash(cur ^ 1);
         __syncthreads();
+    };
+    int t = t_begin;
+    for (; t + 2 <= nt; t += 2) {
+        tile(0, t);
+        tile(1, t + 1);
     }
+    if (t < nt) tile(0, t);
     // register r of block db is X^T[32db + 8(r/4) + 4hh + r%4][key]
     if (key < N) {
 #pragma unroll
