@@ -163,16 +163,15 @@ __global__ void __launch_bounds__(256) fa_bwd_delta_kernel(BwdArgs a) {
 }
 
 // Query rows per dK/dV tile.  d = 64: 32-row tiles keep two workgroups per CU.  d = 128 runs
-// one workgroup per CU with 64-row tiles (two 32-row halves, so that each half's vector work
-// rides on the other half's MFMAs); with dropout, whose mask bits take more registers, 32-row
-// tiles, which fit without spilling.
-template <int D, bool DROP>
-constexpr int bwd_bq() { return D == 128 && !DROP ? 64 : 32; }
+// one workgroup per CU with 64-row tiles, two 32-row halves (without dropout each half's
+// vector work rides on the other half's MFMAs).
+template <int D>
+constexpr int bwd_bq() { return D == 128 ? 64 : 32; }
 
 template <int D, bool CAUSAL, bool PAD, bool DROP = false>
 __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdArgs a) {
     constexpr int BK = 128;        // keys per workgroup (32 per wave)
-    constexpr int BQ = bwd_bq<D, DROP>();  // query rows per tile, handled as 32-row halves
+    constexpr int BQ = bwd_bq<D>();  // query rows per tile, handled as 32-row halves
     constexpr int NH = BQ / 32;
     constexpr int KC = D / 16;     // k-steps over d
     constexpr int NDB = D / 32;    // 32-wide blocks of d
@@ -272,7 +271,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
         f32x16 s[NH], dp[NH];
         // Issue order (without dropout): one slot per k-step with its MFMAs, the LDS operands
         // read two slots ahead, slots kept apart by sched_barrier, so every read has four MFMAs
-        // of time to return; hook(slot) places vector work beside them.  The dropout
+        // of time to return; hook(slot) places vector work beside them.  The d = 64 dropout
         // instantiations, whose mask bits take more registers, keep the compiler's own order
         // (the pinned one would spill there).
         auto sdp_h = [&](int h, auto hook) __attribute__((always_inline)) {
@@ -322,7 +321,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
         auto sdp = [&]() __attribute__((always_inline)) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-                if constexpr (DROP) {
+                if constexpr (DROP && D == 64) {
                     s[h] = dp[h] = f32x16{};
 #pragma unroll
                     for (int c = 0; c < KC; ++c) {
@@ -371,7 +370,7 @@ __global__ void __launch_bounds__(256, D == 64 ? 2 : 1) fa_bwd_dkdv_kernel(BwdAr
                 dsh[r / 8][(r % 8) / 2] = pack_bf16x2(ds[0], ds[1]);
                 dsh[r / 8][(r % 8) / 2 + 1] = pack_bf16x2(ds[2], ds[3]);
             }
-            if constexpr (DROP) {
+            if constexpr (DROP && D == 64) {
 #pragma unroll
                 for (int pc = 0; pc < 2; ++pc)
 #pragma unroll
